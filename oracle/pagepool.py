@@ -1,0 +1,204 @@
+"""Page-table builder, restated in plain Python.
+
+AstrAI docs/guides/inference.md, "KVCache System" (and internals.md, "Cache
+Architecture"):
+
+* contiguous mode: ``req_to_token`` is the linear map
+  slot = req_idx * max_seq_len + pos, nothing is allocated dynamically;
+* paged mode (page_size 1, or larger): a shared pool, slots allocated on demand
+  by a bitmask page allocator with reference counts;
+* with page_size > 1 a radix cache indexes complete token pages as
+  parent-linked edges; a lookup walks from the root comparing each page's
+  exact token tuple, so a page is reused only under the same parent prefix;
+  hashes are kept for introspection and never decide a match; only complete,
+  materialised pages enter it; a new request resumes prefill right after the
+  longest complete-page hit;
+* ``bind_tasks()`` emits ``req_pool_indices``, ``seq_lens``, ``out_cache_loc``
+  (the slots written this step), ``max_len`` (host int), ``kv_indptr`` and
+  ``qo_indptr`` (prefix sums of KV and query lengths) and the query-tile maps
+  ``q_tile_to_batch`` / ``q_tile_to_index``.
+
+Readings where the pages are silent (the allocation order is needed for
+bit-exact tables): request slots and pages are taken lowest-free-first;
+requests are served in the order given and positions in increasing order;
+a logical page maps to physical page ``page_perm[logical]`` when a permutation
+is given; slot = physical_page * page_size + pos % page_size; unused table
+entries are -1; a lookup leaves at least one prompt token to compute, so it
+matches at most floor((n_tokens - 1) / page_size) pages; query tiles are
+request-major, ascending, the last one of a request possibly partial;
+``out_cache_loc`` is flat in ``qo_indptr`` order.
+"""
+
+import numpy as np
+
+
+class PoolError(Exception):
+    """Raised with ``kind`` 'nomem' (pool or request slots exhausted; the state
+    is left unchanged) or 'inval' (bad argument)."""
+
+    def __init__(self, kind: str, msg: str):
+        super().__init__(msg)
+        self.kind = kind
+
+
+class _Node:
+    __slots__ = ("page", "parent", "digest")
+
+    def __init__(self, page, parent, digest):
+        self.page = page
+        self.parent = parent
+        self.digest = digest      # for introspection only
+
+
+class PagePool:
+    def __init__(self, mode: int, pool_slots: int, page_size: int, max_reqs: int,
+                 max_ctx_len: int, page_perm=None):
+        if mode not in (0, 1):
+            raise PoolError("inval", "mode")
+        self.mode = mode
+        self.page_size = 1 if mode == 0 else int(page_size)
+        self.max_reqs = int(max_reqs)
+        self.max_ctx_len = int(max_ctx_len)
+        self.pool_slots = int(pool_slots)
+        if mode == 0 and pool_slots < max_reqs * max_ctx_len:
+            raise PoolError("inval", "contiguous pool too small")
+        if mode == 1 and (page_size < 1 or pool_slots % page_size):
+            raise PoolError("inval", "pool_slots must be a multiple of page_size")
+        self.n_pages = pool_slots // self.page_size if mode == 1 else 0
+        self.perm = None if page_perm is None else [int(x) for x in page_perm]
+        if self.perm is not None and sorted(self.perm) != list(range(self.n_pages)):
+            raise PoolError("inval", "page_perm is not a permutation")
+        self.table = np.full((self.max_reqs, self.max_ctx_len), -1, dtype=np.int32)
+        self.live = [False] * self.max_reqs
+        self.length = [0] * self.max_reqs
+        self.pages = [[] for _ in range(self.max_reqs)]   # logical pages, position order
+        self.free = [True] * self.n_pages
+        self.ref = [0] * self.n_pages
+        self.children = {}                                # (parent id, token tuple) -> node
+        self.root = _Node(None, None, None)
+
+    # -- helpers --------------------------------------------------------------
+    def _slot(self, req: int, pos: int) -> int:
+        if self.mode == 0:
+            return req * self.max_ctx_len + pos
+        lp = self.pages[req][pos // self.page_size]
+        pp = lp if self.perm is None else self.perm[lp]
+        return pp * self.page_size + pos % self.page_size
+
+    def _radix_on(self) -> bool:
+        return self.mode == 1 and self.page_size > 1
+
+    def _page_tokens(self, tokens, k):
+        ps = self.page_size
+        return tuple(int(t) for t in tokens[k * ps:(k + 1) * ps])
+
+    def _check_live(self, req):
+        if not (0 <= req < self.max_reqs) or not self.live[req]:
+            raise PoolError("inval", f"request {req} is not live")
+
+    # -- the calls -------------------------------------------------------------
+    def admit(self, tokens=None, n_tokens: int = 0):
+        """Take the lowest free request slot; match cached pages.  -> (req, cached_len)."""
+        if n_tokens < 0 or n_tokens > self.max_ctx_len:
+            raise PoolError("inval", "n_tokens out of range")
+        try:
+            req = self.live.index(False)
+        except ValueError:
+            raise PoolError("nomem", "no free request slot")
+        matched = []
+        if self._radix_on() and tokens is not None and n_tokens > 0:
+            node = self.root
+            for k in range((n_tokens - 1) // self.page_size):
+                child = self.children.get((id(node), self._page_tokens(tokens, k)))
+                if child is None:
+                    break
+                matched.append(child.page)
+                node = child
+        self.live[req] = True
+        self.pages[req] = list(matched)
+        for p in matched:
+            self.ref[p] += 1
+        n = len(matched) * self.page_size
+        self.length[req] = n
+        for pos in range(n):
+            self.table[req, pos] = self._slot(req, pos)
+        return req, n
+
+    def extend(self, req: int, n_new: int):
+        """Give request ``req`` slots for positions [len, len + n_new)."""
+        self._check_live(req)
+        old = self.length[req]
+        new = old + int(n_new)
+        if n_new < 0 or new > self.max_ctx_len:
+            raise PoolError("inval", "length exceeds max_ctx_len")
+        if self.mode == 1:
+            need = -(-new // self.page_size) - len(self.pages[req])
+            if need > sum(self.free):
+                raise PoolError("nomem", "pool exhausted")
+            for _ in range(max(need, 0)):
+                lp = self.free.index(True)
+                self.free[lp] = False
+                self.ref[lp] = 1
+                self.pages[req].append(lp)
+        self.length[req] = new
+        for pos in range(old, new):
+            self.table[req, pos] = self._slot(req, pos)
+
+    def bind(self, reqs, q_lens, q_tile: int = 64):
+        """Per-step metadata for a batch of live requests."""
+        reqs = [int(r) for r in reqs]
+        q_lens = [int(x) for x in q_lens]
+        if len(reqs) != len(q_lens) or q_tile < 1:
+            raise PoolError("inval", "batch arguments")
+        for r, ql in zip(reqs, q_lens):
+            self._check_live(r)
+            if ql < 0 or ql > self.length[r]:
+                raise PoolError("inval", "q_len exceeds seq_len")
+        seq = [self.length[r] for r in reqs]
+        kv_indptr = [0]
+        qo_indptr = [0]
+        loc = []
+        t2b, t2i = [], []
+        for b, (r, L, ql) in enumerate(zip(reqs, seq, q_lens)):
+            kv_indptr.append(kv_indptr[-1] + L)
+            qo_indptr.append(qo_indptr[-1] + ql)
+            loc.extend(int(self.table[r, p]) for p in range(L - ql, L))
+            for t in range(-(-ql // q_tile)):
+                t2b.append(b)
+                t2i.append(t)
+        i32 = lambda a: np.asarray(a, dtype=np.int32)
+        return dict(req_pool_indices=i32(reqs), seq_lens=i32(seq),
+                    out_cache_loc=i32(loc), kv_indptr=i32(kv_indptr),
+                    qo_indptr=i32(qo_indptr), q_tile_to_batch=i32(t2b),
+                    q_tile_to_index=i32(t2i), num_q_tiles=len(t2b),
+                    max_len=max(seq) if seq else 0)
+
+    def insert(self, req: int, tokens, n_materialized: int):
+        """Record the request's complete, materialised pages in the radix."""
+        self._check_live(req)
+        if not self._radix_on():
+            return
+        n_full = min(int(n_materialized), self.length[req]) // self.page_size
+        node = self.root
+        for k in range(n_full):
+            key = (id(node), self._page_tokens(tokens, k))
+            child = self.children.get(key)
+            if child is None:
+                page = self.pages[req][k]
+                child = _Node(page, node, hash(key[1]))
+                self.children[key] = child
+                self.ref[page] += 1
+            node = child
+
+    def release(self, req: int):
+        """Drop the request's page references and free its request slot."""
+        self._check_live(req)
+        if self.mode == 1:
+            for p in self.pages[req]:
+                self.ref[p] -= 1
+                if self.ref[p] == 0:
+                    self.free[p] = True
+        self.pages[req] = []
+        self.length[req] = 0
+        self.live[req] = False
+        self.table[req, :] = -1
