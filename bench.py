@@ -1,0 +1,195 @@
+"""Benchmark of the paged GQA attention path on one MI355X.
+
+One step = one pass of the whole path over one batch of each headline
+workload, inputs already resident in HBM:
+  decode  (256 requests, page 16, shuffled pages, 24-layer bf16 pool, 16/4
+           heads, d 128, KV lengths log-uniform in [1024, 32768], split 512):
+           rotary write of the new tokens + split-K decode + merge;
+  prefill (16 requests, page 16, radix-cached prefixes 0..2048, extends
+           32..512, 16/4 heads, d 128, bf16):
+           rotary write of the extend tokens + causal prefill.
+The page tables are built once, before timing (they are per-step host
+metadata shared by all layers); their host cost is reported separately.
+
+value = decode KV GB/s: algorithmic bytes (every cached K/V row read once,
+its slot index, q read and output written) / the decode call's device time
+(split-K pass + merge), from HIP events recorded on the stream the kernels
+run on.  The prefill figure (TFLOP/s over unmasked (query, key) pairs) is in
+"prefill".  cpu_baseline times the float64 oracle on a bounded sample of the
+decode workload on the host cores.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+
+
+def decode_bytes(cs) -> int:
+    """Algorithmic bytes of one decode call: K and V rows (all KV heads) of every
+    cached position, its 4-byte slot index, q read and output written."""
+    esz = 2 if cs.dtype == "bf16" else 4
+    row = cs.n_kv_heads * cs.head_dim * esz * 2 + 4
+    return int(cs.seq_lens.sum()) * row + cs.batch * cs.n_heads * cs.head_dim * esz * 2
+
+
+def prefill_flops(cs) -> int:
+    """4*D*Hq per unmasked (query, key) pair: QK^T and PV, 2 flop per MAC."""
+    e, p = cs.new_lens.astype(np.int64), cs.prefix_lens.astype(np.int64)
+    pairs = int((e * p + e * (e + 1) // 2).sum())
+    return 4 * cs.head_dim * cs.n_heads * pairs
+
+
+def cpu_baseline(cs, budget_s: float = 15.0):
+    """The oracle, as it stands, on a bounded sample of the decode workload."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import expect as E
+    from threadpoolctl import threadpool_info
+    rot = E.rotated_new(cs)
+    t0 = time.perf_counter()
+    done, nbytes = [], 0
+    esz = 2
+    for b in range(cs.batch):
+        E.expected_decode(cs, sample=[b], rot=rot)
+        done.append(b)
+        nbytes += int(cs.seq_lens[b]) * (cs.n_kv_heads * cs.head_dim * esz * 2 + 4) + \
+            cs.n_heads * cs.head_dim * esz * 2
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 decode of the first {len(done)} of {cs.batch} requests "
+                      f"({int(cs.seq_lens[done].sum())} KV positions, history regenerated "
+                      f"from the seeded streams), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(requests shard across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import staging
+    from workloads import make_case
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    t_stage = time.perf_counter()
+    cs_d = make_case(5, args.seed)
+    cs_p = make_case(4, args.seed)
+    st_p = staging.stage(cs_p, device=dev, canary=False)
+    st_d = staging.stage(cs_d, device=dev, canary=False)
+    print(f"[bench] staged decode ({cs_d.pool_slots} slots x {cs_d.n_layers} layers) and prefill "
+          f"in {time.perf_counter() - t_stage:.1f} s", file=sys.stderr, flush=True)
+    # host cost of one step's metadata build (decode: every request appends a token)
+    t0 = time.perf_counter()
+    st_d.pool.bind(st_d.reqs, np.ones(cs_d.batch, dtype=np.int32), 64)
+    bind_ms = (time.perf_counter() - t0) * 1e3
+
+    q_dec = staging.decode_query(st_d)
+    out_d = torch.empty_like(q_dec)
+    import paged_gqa_attention_rope_amd as astr
+    o_part, lse_part = astr.decode_workspace(st_d.attn_cache, cs_d.n_heads, cs_d.split_chunk)
+    out_p = torch.empty_like(st_p.q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        staging.run_write(st_d)
+        if ev:
+            ev[1].record(stream)
+        staging.run_decode(st_d, q_dec, out=out_d, o_part=o_part, lse_part=lse_part)
+        if ev:
+            ev[2].record(stream)
+        staging.run_write(st_p)
+        if ev:
+            ev[3].record(stream)
+        staging.run_prefill(st_p, out=out_p)
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
+                      for i in range(args.steps)])             # ms
+    t_wd, t_dec, t_wp, t_pre = parts.mean(axis=0)
+    dbytes = decode_bytes(cs_d)
+    pflops = prefill_flops(cs_p)
+    dec_gbs = dbytes / (t_dec * 1e-3) / 1e9
+    pre_tfs = pflops / (t_pre * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cs_d)
+
+    line = {
+        "metric": "decode attn KV GB/s (% HBM peak) + prefill attn TFLOP/s (% bf16 MFMA peak)",
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cs_d.name,
+            "prefill_workload": cs_p.name,
+            "decode_batch": cs_d.batch, "decode_kv_positions": int(cs_d.seq_lens.sum()),
+            "decode_split_chunk": cs_d.split_chunk, "layer_id": cs_d.layer_id,
+            "prefill_batch": cs_p.batch, "prefill_rows": int(cs_p.new_lens.sum()),
+            "prefill_cached_prefix": int(cs_p.prefix_lens.sum()),
+        },
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_attn (split-K pass + merge)",
+                     "bytes_per_launch": dbytes, "ms_per_launch": round(float(t_dec), 5)},
+        "prefill": {"value": round(pre_tfs, 2), "unit": "TFLOP/s",
+                    "roofline": {"bound": "mfma", "achieved": round(pre_tfs, 2),
+                                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(pre_tfs / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                                 "kernel": "prefill_attn", "flops_per_launch": pflops,
+                                 "ms_per_launch": round(float(t_pre), 5)}},
+        "parts_ms": {"rope_kv_write_decode": round(float(t_wd), 5), "decode_attn": round(float(t_dec), 5),
+                     "rope_kv_write_prefill": round(float(t_wp), 5), "prefill_attn": round(float(t_pre), 5),
+                     "host_bind_decode": round(bind_ms, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,273 @@
+/*
+ * astr.h -- C ABI of the paged grouped-query attention library for AMD
+ * MI355X (gfx950): rotary embedding fused with the KV-cache write, split-K
+ * paged decode attention with its log-sum-exp merge, ragged causal prefill
+ * attention over a paged pool, and the host-side page-table builder.
+ *
+ * Definitions followed (AstrAI documentation pages):
+ *   docs/developer/internals.md -- "Autoregression & Causal Masking",
+ *     "Rotary Position Embedding (RoPE)", "KV Cache Mathematics",
+ *     "Cache Architecture", "Attention Backend".
+ *   docs/guides/inference.md -- "KV Cache", "KVCache System",
+ *     "Attention Backend", "Rotary Embedding Backend".
+ *   AstrAI paper (main.tex) -- "Model Architecture" (GQA, RoPE theta 10 000).
+ *
+ * Conventions shared by every call
+ *   - Device pointers point to memory the caller owns (in practice PyTorch
+ *     tensors).  The library never allocates, frees or synchronises device
+ *     memory; every device call is enqueued on the caller's stream and
+ *     returns without waiting.  `stream` is a hipStream_t (NULL = the
+ *     default stream).
+ *   - Host pointers are read during the call only, except where stated.
+ *   - Every argument is validated on the host before anything is launched.
+ *     On a non-OK return nothing was enqueued and astr_last_error() gives a
+ *     message.  An unsupported dtype or head_dim is an error, never a silent
+ *     switch to another implementation (inference.md, "Attention Backend":
+ *     the kernel wrappers raise instead of falling back, and an explicit
+ *     selection fails rather than switching).
+ *   - Indices read from device metadata are bounds-checked in the kernels:
+ *     a slot outside [0, pool_slots) or a position outside [0, max_pos) is
+ *     skipped (it is neither read nor written), so malformed metadata cannot
+ *     make a kernel touch memory outside the buffers it was given.
+ *   - Layouts are row-major.  q/k/v are [tokens, heads, head_dim] ("blhd"
+ *     with the batch and sequence axes flattened, internals.md "Attention
+ *     Backend"); query head h reads KV head h / (n_heads / n_kv_heads).
+ *   - Supported: kv_dtype in {ASTR_F32, ASTR_BF16}; head_dim in {64, 128};
+ *     n_heads / n_kv_heads in {1, 2, 4, 6, 8}.  Activations (q, out) use
+ *     the pool's dtype; accumulation is float32.
+ */
+#ifndef ASTR_H
+#define ASTR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum astr_status {
+    ASTR_OK = 0,
+    ASTR_E_INVAL = -1,        /* bad argument: null pointer, size or index out of range */
+    ASTR_E_UNSUPPORTED = -2,  /* well-formed but not implemented (dtype, head_dim, group) */
+    ASTR_E_NOMEM = -3,        /* page pool or request slots exhausted; state unchanged */
+    ASTR_E_LAUNCH = -4        /* the HIP runtime rejected a kernel launch */
+} astr_status;
+
+typedef enum astr_dtype { ASTR_F32 = 0, ASTR_BF16 = 1 } astr_dtype;
+
+/*
+ * The per-step view of the KV cache handed to the attention calls: the
+ * fields of the KVCache record (inference.md, "KVCache System").  Pointers
+ * are device pointers; the scalar sizes are host values, so that no call
+ * needs a device-to-host read (max_len is kept on the host for that reason).
+ */
+typedef struct astr_kv_meta {
+    void *k_buffer;                   /* [n_layers, pool_slots, n_kv_heads, head_dim] kv_dtype */
+    void *v_buffer;                   /* same shape and dtype */
+    int64_t pool_slots;               /* token slots per layer */
+    int32_t n_layers;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t kv_dtype;                 /* astr_dtype */
+    const int32_t *req_to_token;      /* [num_reqs, max_ctx_len]: (request, position) -> slot */
+    int32_t num_reqs;
+    int32_t max_ctx_len;              /* row stride of req_to_token */
+    const int32_t *req_pool_indices;  /* [batch]: request row of each batch entry */
+    const int32_t *kv_indptr;         /* [batch + 1]: prefix sum of KV lengths (seq_lens) */
+    const int32_t *qo_indptr;         /* [batch + 1]: prefix sum of query lengths (prefill) */
+    const int32_t *q_tile_to_batch;   /* [num_q_tiles]: query tile -> batch entry (prefill) */
+    const int32_t *q_tile_to_index;   /* [num_q_tiles]: query tile -> tile index in its request */
+    int32_t batch;                    /* host: number of requests in the step */
+    int32_t max_len;                  /* host: max KV length over the batch */
+    int32_t num_q_tiles;              /* host (prefill) */
+    int32_t q_tile;                   /* host (prefill): query rows per tile */
+} astr_kv_meta;
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *astr_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Rotary embedding                                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Fill the rotary cos/sin table (internals.md, "Rotary Position Embedding":
+ * freqs_cis of shape [max_len, dim/2, 2], float32 [cos, sin] pairs).
+ * Entry [pos, i] = (cos(pos * w_i), sin(pos * w_i)) with w_i = theta^(-2i/head_dim)
+ * (RoFormer frequencies, theta from the paper's "Model Architecture" table);
+ * the angle and both functions are evaluated in float64 and rounded to float32.
+ *   freqs_cis  device, [max_pos, head_dim/2, 2] float32, written.
+ * Errors: INVAL (null, max_pos < 1, odd or non-positive head_dim, theta <= 1).
+ */
+int astr_rope_table(float *freqs_cis, int max_pos, int head_dim, double theta, void *stream);
+
+/*
+ * Rotate q and k by their token's position, then write the rotated k and the
+ * unrotated v into the pool row out_cache_loc[t] of layer layer_id:
+ *   k_buffer[layer_id, out_cache_loc[t], h, :] = R(positions[t]) k[t, h, :]
+ *   v_buffer[layer_id, out_cache_loc[t], h, :] = v[t, h, :]
+ *   q[t, h, :] <- R(positions[t]) q[t, h, :]            (in place)
+ * RoPE is applied before the cache write (internals.md, "KV Cache
+ * Mathematics": cached keys keep the rotation of their own position;
+ * inference.md, "KV Cache").  R rotates each adjacent pair (x[2i], x[2i+1])
+ * as the complex product with freqs_cis[pos, i] (inference.md, "Rotary
+ * Embedding Backend": view as complex, multiply, view as real).  Arithmetic
+ * is float32; bf16 results are rounded to nearest-even.
+ *   q              device [n_tokens, n_heads, head_dim] kv_dtype, read and written
+ *   k, v           device [n_tokens, m->n_kv_heads, head_dim] kv_dtype, read
+ *   positions      device [n_tokens] int32, position of each token
+ *   out_cache_loc  device [n_tokens] int32, destination slot of each token
+ *   freqs_cis      device [max_pos, head_dim/2, 2] float32 (astr_rope_table)
+ *   m              host; uses k_buffer, v_buffer, pool_slots, n_layers,
+ *                  n_kv_heads, head_dim, kv_dtype
+ * n_tokens == 0 is a no-op.  Tokens whose slot or position is out of range are
+ * skipped entirely.  Errors: INVAL, UNSUPPORTED, LAUNCH.
+ */
+int astr_rope_kv_write(void *q, const void *k, const void *v,
+                       const int32_t *positions, const int32_t *out_cache_loc,
+                       int n_tokens, int n_heads, const float *freqs_cis, int max_pos,
+                       const astr_kv_meta *m, int layer_id, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention (one query token per request)                          */
+/* ------------------------------------------------------------------------ */
+
+/* Number of KV splits S = ceil(max_len / split_chunk) (0 on bad input). */
+int astr_decode_num_splits(int max_len, int split_chunk);
+
+/*
+ * o[b, h] = sum_j softmax_j(q[b, h] . K_j * sm_scale) V_j over the KV
+ * positions j < L_b of request b, L_b = kv_indptr[b+1] - kv_indptr[b], with
+ * K_j, V_j = k/v_buffer[layer_id, req_to_token[req_pool_indices[b], j], h / G]
+ * (internals.md, "KV Cache Mathematics"; inference.md, "KVCache System":
+ * req_to_token is the page table, one slot per token).  sm_scale <= 0 means
+ * 1/sqrt(head_dim) (internals.md, "Attention Backend").
+ *
+ * Split-K: split s of request b covers positions [s*C, min((s+1)*C, L_b)),
+ * C = split_chunk.  Pass 1 writes, per (b, h, s < ceil(L_b/C)), the split's
+ * normalised output and its natural-log log-sum-exp of scaled scores into
+ * o_part / lse_part (the decode_o_part / decode_ml_part buffers of the
+ * KVCache record, with the split axis made explicit); pass 2 merges them:
+ * M = max_s lse_s, o = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M).
+ * When S == 1 the single pass writes `out` directly and o_part / lse_part
+ * are not touched (they may then be NULL).
+ *   q         device [batch, n_heads, head_dim] kv_dtype (already rotated)
+ *   out       device [batch, n_heads, head_dim] kv_dtype, written
+ *   o_part    device [batch, n_heads, S, head_dim] float32 scratch
+ *   lse_part  device [batch, n_heads, S] float32 scratch
+ *   m         host; uses the pool fields, req_to_token, num_reqs, max_ctx_len,
+ *             req_pool_indices, kv_indptr, batch, max_len (>= every L_b;
+ *             it sizes the split axis and the grid)
+ * Requests with L_b == 0 get a zero output.  Errors: INVAL, UNSUPPORTED, LAUNCH.
+ */
+int astr_decode_attn(const void *q, void *out, int n_heads, const astr_kv_meta *m,
+                     int layer_id, int split_chunk, float sm_scale,
+                     float *o_part, float *lse_part, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Prefill attention (ragged batch, causal, optional cached prefix)        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Causal attention of each request's new tokens over its whole KV range:
+ * request b owns query rows [qo_indptr[b], qo_indptr[b+1]) (e_b of them) and
+ * L_b = kv_indptr[b+1] - kv_indptr[b] keys; its first p_b = L_b - e_b
+ * positions are a cached prefix (inference.md, "KVCache System": a request
+ * resumes after its longest cached page match).  Query i of the request sits
+ * at position p_b + i and sees keys j <= p_b + i (internals.md,
+ * "Autoregression & Causal Masking", aligned to the end of the KV range).
+ * Work is tiled by the query-tile maps q_tile_to_batch / q_tile_to_index:
+ * tile t covers rows [q_tile*idx, min(q_tile*(idx+1), e_b)) of request
+ * q_tile_to_batch[t] (inference.md, "KVCache System").  Keys and values are
+ * read straight from the pool through req_to_token (inference.md, "Attention
+ * Backend": ragged prefill addressed by qo_indptr and kv_indptr).
+ *   q     device [total_q, n_heads, head_dim] kv_dtype (rotated), total_q >=
+ *         qo_indptr[batch]; a tile whose rows fall outside [0, total_q) is skipped
+ *   out   device, same shape and dtype, written (rows of every tile)
+ *   m     host; uses the pool fields, req_to_token, num_reqs, max_ctx_len,
+ *         req_pool_indices, kv_indptr, qo_indptr, q_tile_to_batch,
+ *         q_tile_to_index, batch, max_len, num_q_tiles, q_tile
+ *         (q_tile must be 64)
+ * sm_scale <= 0 means 1/sqrt(head_dim).  Errors: INVAL, UNSUPPORTED, LAUNCH.
+ */
+int astr_prefill_attn(const void *q, void *out, int total_q, int n_heads,
+                      const astr_kv_meta *m, int layer_id, float sm_scale, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Page-table builder (host only; no device calls)                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * PagePool (inference.md, "KVCache System"; internals.md, "Cache
+ * Architecture").  mode 0 = contiguous: slot = req_idx * max_ctx_len + pos,
+ * no dynamic allocation (needs pool_slots >= max_reqs * max_ctx_len).
+ * mode 1 = paged: pages of page_size slots taken from a bitmask allocator
+ * with reference counts; with page_size > 1 a radix cache of complete,
+ * materialised token pages lets a new request reuse an exact page-aligned
+ * prefix (token tuples compared exactly under the same parent page).
+ *
+ * Allocation order (fixed so that tables are reproducible): the lowest free
+ * request slot and the lowest free logical page are taken first; logical
+ * page p maps to physical page page_perm[p] (identity when page_perm is NULL);
+ * slot = physical_page * page_size + pos % page_size.  Unused table entries
+ * hold -1.  A handle is single-threaded and owns host memory only.
+ */
+typedef struct astr_pagepool astr_pagepool;
+
+/* page_perm: host [pool_slots / page_size] permutation, copied; may be NULL.
+ * Errors: INVAL (bad sizes or page_perm not a permutation), NOMEM (host allocation). */
+int astr_pagepool_create(astr_pagepool **out, int mode, int64_t pool_slots, int page_size,
+                         int max_reqs, int max_ctx_len, const int32_t *page_perm);
+void astr_pagepool_destroy(astr_pagepool *pp);
+
+/* Take the lowest free request slot.  With radix sharing on and tokens given
+ * (host [n_tokens]), reuse the longest chain of cached complete pages that
+ * matches tokens[0 : page_size*k], k <= (n_tokens - 1) / page_size (at least
+ * one token is left to compute); *cached_len = page_size * k is then the
+ * request's length.  Errors: INVAL, NOMEM (no free request slot). */
+int astr_pagepool_admit(astr_pagepool *pp, const int32_t *tokens, int n_tokens,
+                        int *req_idx, int *cached_len);
+
+/* Give request req_idx slots for positions [len, len + n_new).
+ * Errors: INVAL (not live, or length > max_ctx_len), NOMEM (pool exhausted;
+ * nothing changes). */
+int astr_pagepool_extend(astr_pagepool *pp, int req_idx, int n_new);
+
+/* Per-step metadata for batch entries b < batch (request req_idx[b], q_lens[b]
+ * new tokens at its last q_lens[b] positions), into caller-owned host arrays:
+ *   seq_lens[batch], out_cache_loc[sum q_lens] (qo order), kv_indptr[batch+1],
+ *   qo_indptr[batch+1], q_tile_to_batch / q_tile_to_index [tile_capacity]
+ *   (tiles of q_tile rows, request-major, ascending; may be NULL when
+ *   tile_capacity is 0), *num_q_tiles, *max_len.
+ * Errors: INVAL (request not live, q_len > seq_len, tile capacity short). */
+int astr_pagepool_bind(astr_pagepool *pp, const int32_t *req_idx, const int32_t *q_lens,
+                       int batch, int q_tile, int32_t *seq_lens, int32_t *out_cache_loc,
+                       int32_t *kv_indptr, int32_t *qo_indptr, int32_t *q_tile_to_batch,
+                       int32_t *q_tile_to_index, int tile_capacity, int *num_q_tiles,
+                       int *max_len);
+
+/* Record the complete pages among the request's first n_materialized
+ * positions (tokens host [n_materialized]) in the radix; partial pages stay
+ * private.  A page already cached under the same parent and tokens is kept
+ * and the request's copy stays private.  No-op without radix sharing. */
+int astr_pagepool_insert(astr_pagepool *pp, int req_idx, const int32_t *tokens,
+                         int n_materialized);
+
+/* Drop the request's page references (pages reaching zero are freed) and
+ * free its request slot; its table row returns to -1. */
+int astr_pagepool_release(astr_pagepool *pp, int req_idx);
+
+/* The host table [max_reqs, max_ctx_len] int32 owned by the handle, valid
+ * until the next call that changes it or destroy (NULL on bad handle). */
+const int32_t *astr_pagepool_table(const astr_pagepool *pp);
+
+/* Introspection: free pages, reference count of a logical page (-1 if out of range). */
+int64_t astr_pagepool_free_pages(const astr_pagepool *pp);
+int astr_pagepool_page_ref(const astr_pagepool *pp, int64_t logical_page);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ASTR_H */

@@ -73,6 +73,8 @@ class PagePool:
         self.length = [0] * self.max_reqs
         self.pages = [[] for _ in range(self.max_reqs)]   # logical pages, position order
         self.free = [True] * self.n_pages
+        self.n_free = self.n_pages
+        self.first_free = 0                               # no free page below this index
         self.ref = [0] * self.n_pages
         self.children = {}                                # (parent id, token tuple) -> node
         self.root = _Node(None, None, None)
@@ -133,10 +135,12 @@ class PagePool:
             raise PoolError("inval", "length exceeds max_ctx_len")
         if self.mode == 1:
             need = -(-new // self.page_size) - len(self.pages[req])
-            if need > sum(self.free):
+            if need > self.n_free:
                 raise PoolError("nomem", "pool exhausted")
             for _ in range(max(need, 0)):
-                lp = self.free.index(True)
+                lp = self.free.index(True, self.first_free)
+                self.first_free = lp + 1
+                self.n_free -= 1
                 self.free[lp] = False
                 self.ref[lp] = 1
                 self.pages[req].append(lp)
@@ -198,6 +202,8 @@ class PagePool:
                 self.ref[p] -= 1
                 if self.ref[p] == 0:
                     self.free[p] = True
+                    self.n_free += 1
+                    self.first_free = min(self.first_free, p)
         self.pages[req] = []
         self.length[req] = 0
         self.live[req] = False

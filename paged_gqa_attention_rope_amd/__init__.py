@@ -1,0 +1,13 @@
+"""Paged grouped-query attention with rotary embeddings for AMD MI355X (gfx950).
+
+The compute lives in libastr.so (hand-written HIP kernels behind the C ABI in
+include/astr.h); this package is its Python binding.  Importing it does not
+touch the GPU; the library is loaded on first use and a missing library is an
+error, never a fallback.
+"""
+
+from .api import (  # noqa: F401
+    KVCache, PagePool, cache_from_bind, decode_attn, decode_num_splits, decode_workspace,
+    prefill_attn, rope_kv_write, rope_table,
+)
+from ._lib import AstrArgError, AstrError, LIB_PATH  # noqa: F401

@@ -1,0 +1,194 @@
+// The C entry points of libastr: argument validation, then one launcher call
+// on the caller's stream.  Nothing here allocates, frees or synchronises
+// device memory, and no call switches to another implementation when a shape
+// or dtype is unsupported -- it returns an error instead.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "astr.h"
+#include "kernels.hpp"
+#include "status.hpp"
+
+namespace astr {
+
+namespace {
+thread_local char g_err[512] = "";
+}
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634074;
+
+bool group_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 6 || g == 8; }
+
+// Checks shared by every attention-side call; fills the layer view.
+int check_pool(const char *who, const astr_kv_meta *m, int n_heads, int layer_id, PoolView &pv) {
+    if (!m) return fail(ASTR_E_INVAL, "%s: null meta", who);
+    if (m->kv_dtype != ASTR_F32 && m->kv_dtype != ASTR_BF16)
+        return fail(ASTR_E_UNSUPPORTED, "%s: kv_dtype %d (supported: f32, bf16)", who, m->kv_dtype);
+    if (m->head_dim != 64 && m->head_dim != 128)
+        return fail(ASTR_E_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", who, m->head_dim);
+    if (m->n_kv_heads < 1 || n_heads < 1 || n_heads % m->n_kv_heads != 0)
+        return fail(ASTR_E_INVAL, "%s: n_heads %d is not a multiple of n_kv_heads %d", who, n_heads,
+                    m->n_kv_heads);
+    if (!group_supported(n_heads / m->n_kv_heads))
+        return fail(ASTR_E_UNSUPPORTED, "%s: %d query heads per KV head (supported: 1, 2, 4, 6, 8)", who,
+                    n_heads / m->n_kv_heads);
+    if (m->n_kv_heads > 65535) return fail(ASTR_E_UNSUPPORTED, "%s: too many KV heads", who);
+    if (!m->k_buffer || !m->v_buffer || m->pool_slots < 1 || m->n_layers < 1)
+        return fail(ASTR_E_INVAL, "%s: empty pool", who);
+    if (layer_id < 0 || layer_id >= m->n_layers)
+        return fail(ASTR_E_INVAL, "%s: layer_id %d outside [0, %d)", who, layer_id, m->n_layers);
+    const size_t esz = m->kv_dtype == ASTR_BF16 ? 2 : 4;
+    const size_t layer_bytes = static_cast<size_t>(m->pool_slots) * m->n_kv_heads * m->head_dim * esz;
+    pv.k_layer = static_cast<char *>(m->k_buffer) + layer_bytes * layer_id;
+    pv.v_layer = static_cast<char *>(m->v_buffer) + layer_bytes * layer_id;
+    pv.pool_slots = m->pool_slots;
+    pv.n_kv_heads = m->n_kv_heads;
+    pv.head_dim = m->head_dim;
+    pv.dtype = m->kv_dtype;
+    return ASTR_OK;
+}
+
+int check_table(const char *who, const astr_kv_meta *m) {
+    if (m->batch < 0) return fail(ASTR_E_INVAL, "%s: batch %d", who, m->batch);
+    if (m->batch == 0) return ASTR_OK;
+    if (!m->req_to_token || !m->req_pool_indices || !m->kv_indptr || m->num_reqs < 1 ||
+        m->max_ctx_len < 1)
+        return fail(ASTR_E_INVAL, "%s: missing request table", who);
+    if (m->max_len < 0 || m->max_len > m->max_ctx_len)
+        return fail(ASTR_E_INVAL, "%s: max_len %d outside [0, max_ctx_len %d]", who, m->max_len,
+                    m->max_ctx_len);
+    return ASTR_OK;
+}
+
+int launched(const char *who, hipError_t e) {
+    if (e != hipSuccess) return fail(ASTR_E_LAUNCH, "%s: %s", who, hipGetErrorString(e));
+    return ASTR_OK;
+}
+
+float scale_of(float sm_scale, int head_dim) {
+    const double s = sm_scale > 0.f ? static_cast<double>(sm_scale) : 1.0 / std::sqrt(static_cast<double>(head_dim));
+    return static_cast<float>(s * kLog2e);
+}
+
+}  // namespace
+}  // namespace astr
+
+using astr::fail;
+
+extern "C" const char *astr_last_error(void) { return astr::g_err; }
+
+extern "C" int astr_rope_table(float *freqs_cis, int max_pos, int head_dim, double theta, void *stream) {
+    if (!freqs_cis || max_pos < 1 || head_dim < 2 || head_dim % 2 || !(theta > 1.0))
+        return fail(ASTR_E_INVAL, "rope_table: bad argument");
+    return astr::launched("rope_table",
+                          astr::launch_rope_table(freqs_cis, max_pos, head_dim, theta,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int astr_rope_kv_write(void *q, const void *k, const void *v, const int32_t *positions,
+                                  const int32_t *out_cache_loc, int n_tokens, int n_heads,
+                                  const float *freqs_cis, int max_pos, const astr_kv_meta *m,
+                                  int layer_id, void *stream) {
+    astr::RopeArgs a{};
+    int st = astr::check_pool("rope_kv_write", m, n_heads, layer_id, a.pool);
+    if (st) return st;
+    if (n_tokens < 0) return fail(ASTR_E_INVAL, "rope_kv_write: n_tokens %d", n_tokens);
+    if (n_tokens == 0) return ASTR_OK;
+    if (!q || !k || !v || !positions || !out_cache_loc || !freqs_cis || max_pos < 1)
+        return fail(ASTR_E_INVAL, "rope_kv_write: null argument or max_pos < 1");
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.positions = positions;
+    a.out_cache_loc = out_cache_loc;
+    a.n_tokens = n_tokens;
+    a.n_heads = n_heads;
+    a.freqs = freqs_cis;
+    a.max_pos = max_pos;
+    return astr::launched("rope_kv_write", astr::launch_rope_kv_write(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int astr_decode_num_splits(int max_len, int split_chunk) {
+    if (max_len < 0 || split_chunk < 1) return 0;
+    const int s = (max_len + split_chunk - 1) / split_chunk;
+    return s < 1 ? 1 : s;
+}
+
+extern "C" int astr_decode_attn(const void *q, void *out, int n_heads, const astr_kv_meta *m,
+                                int layer_id, int split_chunk, float sm_scale, float *o_part,
+                                float *lse_part, void *stream) {
+    astr::DecodeArgs a{};
+    int st = astr::check_pool("decode_attn", m, n_heads, layer_id, a.pool);
+    if (st) return st;
+    st = astr::check_table("decode_attn", m);
+    if (st) return st;
+    if (m->batch == 0) return ASTR_OK;
+    if (!q || !out) return fail(ASTR_E_INVAL, "decode_attn: null q or out");
+    if (split_chunk < 1) return fail(ASTR_E_INVAL, "decode_attn: split_chunk %d", split_chunk);
+    const int ns = astr_decode_num_splits(m->max_len, split_chunk);
+    if (ns > 1 && (!o_part || !lse_part))
+        return fail(ASTR_E_INVAL, "decode_attn: %d splits need o_part and lse_part", ns);
+    if (static_cast<int64_t>(m->batch) * ns * m->n_kv_heads > INT32_MAX)
+        return fail(ASTR_E_UNSUPPORTED, "decode_attn: grid too large");
+    a.q = q;
+    a.out = out;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.req_to_token = m->req_to_token;
+    a.num_reqs = m->num_reqs;
+    a.max_ctx_len = m->max_ctx_len;
+    a.req_pool_indices = m->req_pool_indices;
+    a.kv_indptr = m->kv_indptr;
+    a.batch = m->batch;
+    a.n_heads = n_heads;
+    a.split_chunk = split_chunk;
+    a.n_splits = ns;
+    a.scale_log2 = astr::scale_of(sm_scale, m->head_dim);
+    return astr::launched("decode_attn", astr::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int astr_prefill_attn(const void *q, void *out, int total_q, int n_heads,
+                                 const astr_kv_meta *m, int layer_id, float sm_scale, void *stream) {
+    astr::PrefillArgs a{};
+    int st = astr::check_pool("prefill_attn", m, n_heads, layer_id, a.pool);
+    if (st) return st;
+    st = astr::check_table("prefill_attn", m);
+    if (st) return st;
+    if (m->batch == 0 || m->num_q_tiles == 0) return ASTR_OK;
+    if (m->num_q_tiles < 0) return fail(ASTR_E_INVAL, "prefill_attn: num_q_tiles %d", m->num_q_tiles);
+    if (m->q_tile != 64) return fail(ASTR_E_UNSUPPORTED, "prefill_attn: q_tile %d (supported: 64)", m->q_tile);
+    if (!q || !out || !m->qo_indptr || !m->q_tile_to_batch || !m->q_tile_to_index)
+        return fail(ASTR_E_INVAL, "prefill_attn: null q, out or tile metadata");
+    if (n_heads > 65535) return fail(ASTR_E_UNSUPPORTED, "prefill_attn: too many heads");
+    if (total_q < 0) return fail(ASTR_E_INVAL, "prefill_attn: total_q %d", total_q);
+    a.q = q;
+    a.total_q = total_q;
+    a.out = out;
+    a.req_to_token = m->req_to_token;
+    a.num_reqs = m->num_reqs;
+    a.max_ctx_len = m->max_ctx_len;
+    a.req_pool_indices = m->req_pool_indices;
+    a.qo_indptr = m->qo_indptr;
+    a.kv_indptr = m->kv_indptr;
+    a.q_tile_to_batch = m->q_tile_to_batch;
+    a.q_tile_to_index = m->q_tile_to_index;
+    a.batch = m->batch;
+    a.num_q_tiles = m->num_q_tiles;
+    a.q_tile = m->q_tile;
+    a.n_heads = n_heads;
+    a.scale_log2 = astr::scale_of(sm_scale, m->head_dim);
+    return astr::launched("prefill_attn", astr::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}

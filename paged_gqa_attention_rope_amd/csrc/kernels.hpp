@@ -1,0 +1,75 @@
+// Host-side launchers of the HIP kernels (one translation unit per kernel
+// family).  Arguments have been validated by the C entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace astr {
+
+struct PoolView {
+    void *k_layer;          // k_buffer + layer_id * pool_slots * n_kv_heads * head_dim
+    void *v_layer;
+    int64_t pool_slots;
+    int n_kv_heads;
+    int head_dim;
+    int dtype;              // astr_dtype
+};
+
+struct RopeArgs {
+    void *q;
+    const void *k;
+    const void *v;
+    const int32_t *positions;
+    const int32_t *out_cache_loc;
+    int n_tokens;
+    int n_heads;
+    const float *freqs;
+    int max_pos;
+    PoolView pool;
+};
+
+struct DecodeArgs {
+    const void *q;
+    void *out;
+    float *o_part;
+    float *lse_part;
+    PoolView pool;
+    const int32_t *req_to_token;
+    int num_reqs;
+    int max_ctx_len;
+    const int32_t *req_pool_indices;
+    const int32_t *kv_indptr;
+    int batch;
+    int n_heads;
+    int split_chunk;
+    int n_splits;
+    float scale_log2;       // sm_scale * log2(e)
+};
+
+struct PrefillArgs {
+    const void *q;
+    void *out;
+    int total_q;            // rows of q and out
+    PoolView pool;
+    const int32_t *req_to_token;
+    int num_reqs;
+    int max_ctx_len;
+    const int32_t *req_pool_indices;
+    const int32_t *qo_indptr;
+    const int32_t *kv_indptr;
+    const int32_t *q_tile_to_batch;
+    const int32_t *q_tile_to_index;
+    int batch;
+    int num_q_tiles;
+    int q_tile;
+    int n_heads;
+    float scale_log2;
+};
+
+hipError_t launch_rope_table(float *freqs, int max_pos, int head_dim, double theta, hipStream_t s);
+hipError_t launch_rope_kv_write(const RopeArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+
+}  // namespace astr

@@ -1,0 +1,336 @@
+// Host page-table builder: KVStorage slot allocation, the request-to-token
+// table, reference-counted pages and the exact page-aligned radix cache
+// (AstrAI docs/guides/inference.md, "KVCache System"; docs/developer/
+// internals.md, "Cache Architecture").  Host memory only; no device calls.
+//
+// Allocation is deterministic: lowest free request slot, lowest free logical
+// page (a bitmask scanned word by word), logical -> physical through an
+// optional permutation.  The radix keys a child by (parent node, 64-bit FNV-1a
+// digest of the page's tokens) only to find candidates; a match always
+// compares the stored token tuple exactly, so the digest never decides it.
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "astr.h"
+#include "status.hpp"
+
+namespace {
+
+struct Node {
+    int32_t page;                 // logical page id
+    int32_t parent;               // node index, -1 for children of the root
+    uint64_t digest;              // FNV-1a of the page's tokens (introspection, bucketing)
+    std::vector<int32_t> tokens;  // the exact page contents
+};
+
+struct KeyHash {
+    size_t operator()(const std::pair<int32_t, uint64_t> &k) const {
+        return static_cast<size_t>(k.second ^ (static_cast<uint64_t>(k.first) * 0x9E3779B97F4A7C15ull));
+    }
+};
+
+uint64_t fnv1a(const int32_t *t, int n) {
+    uint64_t h = 0xcbf29ce484222325ull;
+    for (int i = 0; i < n; ++i) {
+        uint32_t x = static_cast<uint32_t>(t[i]);
+        for (int b = 0; b < 4; ++b) {
+            h ^= (x >> (8 * b)) & 0xffu;
+            h *= 0x100000001b3ull;
+        }
+    }
+    return h;
+}
+
+}  // namespace
+
+struct astr_pagepool {
+    int mode = 0;
+    int page_size = 1;
+    int max_reqs = 0;
+    int max_ctx_len = 0;
+    int64_t pool_slots = 0;
+    int64_t n_pages = 0;
+    std::vector<int32_t> perm;            // logical -> physical (empty = identity)
+    std::vector<int32_t> table;           // [max_reqs, max_ctx_len]
+    std::vector<uint8_t> live;
+    std::vector<int32_t> length;
+    std::vector<std::vector<int32_t>> pages;   // logical pages of each request, in position order
+    std::vector<uint64_t> free_bits;      // bit set = page free
+    int64_t free_count = 0;
+    int64_t free_hint = 0;                // no free page below word free_hint
+    std::vector<int32_t> ref;
+    std::vector<Node> nodes;
+    std::unordered_map<std::pair<int32_t, uint64_t>, std::vector<int32_t>, KeyHash> children;
+
+    bool radix_on() const { return mode == 1 && page_size > 1; }
+
+    int64_t slot_of(int req, int pos) const {
+        if (mode == 0) return static_cast<int64_t>(req) * max_ctx_len + pos;
+        int32_t lp = pages[req][pos / page_size];
+        int64_t pp = perm.empty() ? lp : perm[lp];
+        return pp * page_size + pos % page_size;
+    }
+
+    int64_t take_lowest_page() {
+        for (int64_t w = free_hint; w < static_cast<int64_t>(free_bits.size()); ++w) {
+            if (free_bits[w]) {
+                int bit = __builtin_ctzll(free_bits[w]);
+                free_bits[w] &= ~(1ull << bit);
+                free_hint = w;
+                --free_count;
+                return w * 64 + bit;
+            }
+        }
+        return -1;
+    }
+
+    void give_back_page(int64_t p) {
+        free_bits[p / 64] |= 1ull << (p % 64);
+        if (p / 64 < free_hint) free_hint = p / 64;
+        ++free_count;
+    }
+
+    int find_child(int32_t parent, const int32_t *tok) const {
+        auto it = children.find({parent, fnv1a(tok, page_size)});
+        if (it == children.end()) return -1;
+        for (int32_t n : it->second) {
+            if (std::memcmp(nodes[n].tokens.data(), tok, sizeof(int32_t) * page_size) == 0) return n;
+        }
+        return -1;
+    }
+};
+
+static int check_live(const astr_pagepool *pp, int req) {
+    if (!pp) return astr::fail(ASTR_E_INVAL, "pagepool: null handle");
+    if (req < 0 || req >= pp->max_reqs || !pp->live[req])
+        return astr::fail(ASTR_E_INVAL, "pagepool: request %d is not live", req);
+    return ASTR_OK;
+}
+
+extern "C" int astr_pagepool_create(astr_pagepool **out, int mode, int64_t pool_slots, int page_size,
+                                    int max_reqs, int max_ctx_len, const int32_t *page_perm) {
+    if (!out) return astr::fail(ASTR_E_INVAL, "pagepool_create: null out");
+    *out = nullptr;
+    if (mode != 0 && mode != 1) return astr::fail(ASTR_E_INVAL, "pagepool_create: mode %d", mode);
+    if (max_reqs < 1 || max_ctx_len < 1 || pool_slots < 1)
+        return astr::fail(ASTR_E_INVAL, "pagepool_create: sizes must be positive");
+    if (mode == 0 && pool_slots < static_cast<int64_t>(max_reqs) * max_ctx_len)
+        return astr::fail(ASTR_E_INVAL, "pagepool_create: contiguous pool needs max_reqs*max_ctx_len slots");
+    if (mode == 1 && (page_size < 1 || pool_slots % page_size != 0))
+        return astr::fail(ASTR_E_INVAL, "pagepool_create: pool_slots must be a multiple of page_size");
+    if (mode == 1 && pool_slots / page_size > INT32_MAX)
+        return astr::fail(ASTR_E_INVAL, "pagepool_create: too many pages");
+    astr_pagepool *pp = new (std::nothrow) astr_pagepool();
+    if (!pp) return astr::fail(ASTR_E_NOMEM, "pagepool_create: host allocation");
+    try {
+        pp->mode = mode;
+        pp->page_size = mode == 0 ? 1 : page_size;
+        pp->max_reqs = max_reqs;
+        pp->max_ctx_len = max_ctx_len;
+        pp->pool_slots = pool_slots;
+        pp->n_pages = mode == 1 ? pool_slots / page_size : 0;
+        pp->table.assign(static_cast<size_t>(max_reqs) * max_ctx_len, -1);
+        pp->live.assign(max_reqs, 0);
+        pp->length.assign(max_reqs, 0);
+        pp->pages.assign(max_reqs, {});
+        if (mode == 1) {
+            pp->free_bits.assign((pp->n_pages + 63) / 64, 0);
+            for (int64_t p = 0; p < pp->n_pages; ++p) pp->free_bits[p / 64] |= 1ull << (p % 64);
+            pp->free_count = pp->n_pages;
+            pp->ref.assign(pp->n_pages, 0);
+            if (page_perm) {
+                pp->perm.assign(page_perm, page_perm + pp->n_pages);
+                std::vector<uint8_t> seen(pp->n_pages, 0);
+                for (int64_t i = 0; i < pp->n_pages; ++i) {
+                    int32_t x = pp->perm[i];
+                    if (x < 0 || x >= pp->n_pages || seen[x]) {
+                        delete pp;
+                        return astr::fail(ASTR_E_INVAL, "pagepool_create: page_perm is not a permutation");
+                    }
+                    seen[x] = 1;
+                }
+            }
+        }
+    } catch (const std::bad_alloc &) {
+        delete pp;
+        return astr::fail(ASTR_E_NOMEM, "pagepool_create: host allocation");
+    }
+    *out = pp;
+    return ASTR_OK;
+}
+
+extern "C" void astr_pagepool_destroy(astr_pagepool *pp) { delete pp; }
+
+extern "C" int astr_pagepool_admit(astr_pagepool *pp, const int32_t *tokens, int n_tokens,
+                                   int *req_idx, int *cached_len) {
+    if (!pp || !req_idx || !cached_len) return astr::fail(ASTR_E_INVAL, "pagepool_admit: null argument");
+    if (n_tokens < 0 || n_tokens > pp->max_ctx_len)
+        return astr::fail(ASTR_E_INVAL, "pagepool_admit: n_tokens %d outside [0, %d]", n_tokens, pp->max_ctx_len);
+    int req = -1;
+    for (int r = 0; r < pp->max_reqs; ++r) {
+        if (!pp->live[r]) { req = r; break; }
+    }
+    if (req < 0) return astr::fail(ASTR_E_NOMEM, "pagepool_admit: no free request slot");
+    std::vector<int32_t> matched;
+    if (pp->radix_on() && tokens && n_tokens > 0) {
+        int32_t parent = -1;
+        int max_pages = (n_tokens - 1) / pp->page_size;
+        for (int k = 0; k < max_pages; ++k) {
+            int n = pp->find_child(parent, tokens + static_cast<size_t>(k) * pp->page_size);
+            if (n < 0) break;
+            matched.push_back(pp->nodes[n].page);
+            parent = n;
+        }
+    }
+    pp->live[req] = 1;
+    pp->pages[req] = matched;
+    for (int32_t p : matched) ++pp->ref[p];
+    int len = static_cast<int>(matched.size()) * pp->page_size;
+    pp->length[req] = len;
+    int32_t *row = pp->table.data() + static_cast<size_t>(req) * pp->max_ctx_len;
+    for (int pos = 0; pos < len; ++pos) row[pos] = static_cast<int32_t>(pp->slot_of(req, pos));
+    *req_idx = req;
+    *cached_len = len;
+    return ASTR_OK;
+}
+
+extern "C" int astr_pagepool_extend(astr_pagepool *pp, int req_idx, int n_new) {
+    int st = check_live(pp, req_idx);
+    if (st) return st;
+    int old = pp->length[req_idx];
+    if (n_new < 0 || static_cast<int64_t>(old) + n_new > pp->max_ctx_len)
+        return astr::fail(ASTR_E_INVAL, "pagepool_extend: length %lld exceeds max_ctx_len %d",
+                          static_cast<long long>(old) + n_new, pp->max_ctx_len);
+    int nw = old + n_new;
+    if (pp->mode == 1) {
+        int64_t need = (static_cast<int64_t>(nw) + pp->page_size - 1) / pp->page_size -
+                       static_cast<int64_t>(pp->pages[req_idx].size());
+        if (need > pp->free_count)
+            return astr::fail(ASTR_E_NOMEM, "pagepool_extend: need %lld pages, %lld free",
+                              static_cast<long long>(need), static_cast<long long>(pp->free_count));
+        for (int64_t i = 0; i < need; ++i) {
+            int64_t lp = pp->take_lowest_page();
+            pp->ref[lp] = 1;
+            pp->pages[req_idx].push_back(static_cast<int32_t>(lp));
+        }
+    }
+    pp->length[req_idx] = nw;
+    int32_t *row = pp->table.data() + static_cast<size_t>(req_idx) * pp->max_ctx_len;
+    for (int pos = old; pos < nw; ++pos) row[pos] = static_cast<int32_t>(pp->slot_of(req_idx, pos));
+    return ASTR_OK;
+}
+
+extern "C" int astr_pagepool_bind(astr_pagepool *pp, const int32_t *req_idx, const int32_t *q_lens,
+                                  int batch, int q_tile, int32_t *seq_lens, int32_t *out_cache_loc,
+                                  int32_t *kv_indptr, int32_t *qo_indptr, int32_t *q_tile_to_batch,
+                                  int32_t *q_tile_to_index, int tile_capacity, int *num_q_tiles,
+                                  int *max_len) {
+    if (!pp || batch < 0 || (batch > 0 && (!req_idx || !q_lens)) || !seq_lens || !kv_indptr ||
+        !qo_indptr || !num_q_tiles || !max_len || q_tile < 1 || tile_capacity < 0)
+        return astr::fail(ASTR_E_INVAL, "pagepool_bind: bad argument");
+    if (tile_capacity > 0 && (!q_tile_to_batch || !q_tile_to_index))
+        return astr::fail(ASTR_E_INVAL, "pagepool_bind: null tile arrays");
+    int64_t n_tiles = 0, total_q = 0;
+    for (int b = 0; b < batch; ++b) {
+        int st = check_live(pp, req_idx[b]);
+        if (st) return st;
+        if (q_lens[b] < 0 || q_lens[b] > pp->length[req_idx[b]])
+            return astr::fail(ASTR_E_INVAL, "pagepool_bind: q_len %d of entry %d exceeds its length %d",
+                              q_lens[b], b, pp->length[req_idx[b]]);
+        n_tiles += (q_lens[b] + q_tile - 1) / q_tile;
+        total_q += q_lens[b];
+    }
+    if (total_q > 0 && !out_cache_loc) return astr::fail(ASTR_E_INVAL, "pagepool_bind: null out_cache_loc");
+    if (tile_capacity > 0 && n_tiles > tile_capacity)
+        return astr::fail(ASTR_E_INVAL, "pagepool_bind: %lld tiles exceed capacity %d",
+                          static_cast<long long>(n_tiles), tile_capacity);
+    kv_indptr[0] = 0;
+    qo_indptr[0] = 0;
+    int mx = 0, t = 0;
+    int64_t w = 0;
+    for (int b = 0; b < batch; ++b) {
+        int r = req_idx[b];
+        int L = pp->length[r];
+        int ql = q_lens[b];
+        seq_lens[b] = L;
+        kv_indptr[b + 1] = kv_indptr[b] + L;
+        qo_indptr[b + 1] = qo_indptr[b] + ql;
+        if (L > mx) mx = L;
+        const int32_t *row = pp->table.data() + static_cast<size_t>(r) * pp->max_ctx_len;
+        for (int pos = L - ql; pos < L; ++pos) out_cache_loc[w++] = row[pos];
+        if (tile_capacity > 0) {
+            for (int i = 0; i * q_tile < ql; ++i, ++t) {
+                q_tile_to_batch[t] = b;
+                q_tile_to_index[t] = i;
+            }
+        }
+    }
+    *num_q_tiles = static_cast<int>(n_tiles);
+    *max_len = mx;
+    return ASTR_OK;
+}
+
+extern "C" int astr_pagepool_insert(astr_pagepool *pp, int req_idx, const int32_t *tokens,
+                                    int n_materialized) {
+    int st = check_live(pp, req_idx);
+    if (st) return st;
+    if (!pp->radix_on()) return ASTR_OK;
+    if (n_materialized < 0 || (n_materialized > 0 && !tokens))
+        return astr::fail(ASTR_E_INVAL, "pagepool_insert: bad tokens");
+    int n = n_materialized < pp->length[req_idx] ? n_materialized : pp->length[req_idx];
+    int full = n / pp->page_size;
+    int32_t parent = -1;
+    try {
+        for (int k = 0; k < full; ++k) {
+            const int32_t *tok = tokens + static_cast<size_t>(k) * pp->page_size;
+            int c = pp->find_child(parent, tok);
+            if (c < 0) {
+                Node nd;
+                nd.page = pp->pages[req_idx][k];
+                nd.parent = parent;
+                nd.digest = fnv1a(tok, pp->page_size);
+                nd.tokens.assign(tok, tok + pp->page_size);
+                c = static_cast<int>(pp->nodes.size());
+                pp->nodes.push_back(std::move(nd));
+                pp->children[{parent, pp->nodes.back().digest}].push_back(c);
+                ++pp->ref[pp->nodes.back().page];
+            }
+            parent = c;
+        }
+    } catch (const std::bad_alloc &) {
+        return astr::fail(ASTR_E_NOMEM, "pagepool_insert: host allocation");
+    }
+    return ASTR_OK;
+}
+
+extern "C" int astr_pagepool_release(astr_pagepool *pp, int req_idx) {
+    int st = check_live(pp, req_idx);
+    if (st) return st;
+    if (pp->mode == 1) {
+        for (int32_t p : pp->pages[req_idx]) {
+            if (--pp->ref[p] == 0) pp->give_back_page(p);
+        }
+    }
+    pp->pages[req_idx].clear();
+    pp->length[req_idx] = 0;
+    pp->live[req_idx] = 0;
+    int32_t *row = pp->table.data() + static_cast<size_t>(req_idx) * pp->max_ctx_len;
+    for (int i = 0; i < pp->max_ctx_len; ++i) row[i] = -1;
+    return ASTR_OK;
+}
+
+extern "C" const int32_t *astr_pagepool_table(const astr_pagepool *pp) {
+    return pp ? pp->table.data() : nullptr;
+}
+
+extern "C" int64_t astr_pagepool_free_pages(const astr_pagepool *pp) {
+    return pp ? pp->free_count : -1;
+}
+
+extern "C" int astr_pagepool_page_ref(const astr_pagepool *pp, int64_t logical_page) {
+    if (!pp || logical_page < 0 || logical_page >= pp->n_pages) return -1;
+    return pp->ref[logical_page];
+}

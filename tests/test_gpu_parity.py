@@ -1,0 +1,284 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Every case is drawn by ``workloads`` with a fixed seed; the GPU side is staged
+by ``staging`` (library page tables, torch-allocated pool pre-filled with a
+NaN canary), the expected side by ``expect`` (oracle only).  Bars: page
+tables bit-exact (covered on the CPU in test_native_host), rotated K within
+1 bf16 ulp, V copied bit-exactly, outputs within max-abs 1e-5 (float32) or
+max-abs 2e-2 and rel-L2 1e-2 (bf16).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import expect as E
+import paged_gqa_attention_rope_amd as astr
+import staging
+from oracle import attention as A
+from oracle import rope
+from workloads import make_case
+from workloads.gen import decode_case, prefill_case
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+@pytest.fixture(autouse=True)
+def _cleanup():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# cases
+# ---------------------------------------------------------------------------
+
+def _dec(seed, **kw):
+    base = dict(batch=6, n_heads=16, n_kv_heads=4, head_dim=128, dtype="bf16", mode=1,
+                page_size=16, split_chunk=256, len_lo=1, len_hi=1500, shuffle_pages=True)
+    base.update(kw)
+    return decode_case(seed, **base)
+
+
+def _pre(seed, **kw):
+    base = dict(batch=5, n_heads=16, n_kv_heads=4, head_dim=128, dtype="bf16", mode=0,
+                page_size=1, q_tile=64, ext_lo=1, ext_hi=200)
+    base.update(kw)
+    return prefill_case(seed, **base)
+
+
+DECODE = {
+    "cfg1": lambda: make_case(1),
+    "cfg2": lambda: make_case(2),
+    "cfg2-seed101": lambda: make_case(2, 101),
+    "page16-3layers-chunk512": lambda: _dec(11, batch=12, split_chunk=512, len_hi=3000,
+                                            log_uniform=True, n_layers=3, random_layer=True),
+    "single-split-direct": lambda: _dec(12, batch=5, split_chunk=256, len_hi=256, page_size=1,
+                                        pool_slots=4096),
+    "length-one-and-two": lambda: _dec(13, lens=[1, 1, 2, 3, 300, 257], split_chunk=128),
+    "g1-d64-contig": lambda: _dec(14, batch=4, n_heads=8, n_kv_heads=8, head_dim=64, mode=0,
+                                  split_chunk=128, len_lo=100, len_hi=700, shuffle_pages=False),
+    "g6-d64": lambda: _dec(15, n_heads=24, n_kv_heads=4, head_dim=64, split_chunk=300),
+    "g8-d128": lambda: _dec(16, n_heads=16, n_kv_heads=2, split_chunk=200),
+    "g2-d128-f32": lambda: _dec(17, n_heads=8, n_kv_heads=4, dtype="f32", split_chunk=100),
+    "g4-d64-f32-page1": lambda: _dec(18, head_dim=64, dtype="f32", page_size=1, pool_slots=20000),
+}
+
+PREFILL = {
+    "cfg3": lambda: make_case(3),
+    "cfg4": lambda: make_case(4),
+    "cfg4-seed101": lambda: make_case(4, 101),
+    "tiny-extends": lambda: _pre(21, batch=7, ext_lo=1, ext_hi=3),
+    "ragged-65-129": lambda: _pre(22, batch=3, ext_lo=63, ext_hi=130),
+    "prefix-page16-g1-d64": lambda: _pre(23, n_heads=4, n_kv_heads=4, head_dim=64, mode=1,
+                                         page_size=16, pool_slots=16384, n_groups=2,
+                                         prefix_pages_hi=20, ext_lo=1, ext_hi=150,
+                                         max_ctx_len=480),
+    "prefix-g6-d64": lambda: _pre(24, n_heads=24, n_kv_heads=4, head_dim=64, mode=1,
+                                  page_size=16, pool_slots=16384, n_groups=3, prefix_pages_hi=30,
+                                  ext_lo=10, ext_hi=140, max_ctx_len=640),
+    "prefix-g8-d128": lambda: _pre(25, n_heads=16, n_kv_heads=2, mode=1, page_size=16,
+                                   pool_slots=16384, n_groups=2, prefix_pages_hi=12, ext_hi=100,
+                                   max_ctx_len=300),
+    "g2-f32-d128": lambda: _pre(26, n_heads=8, n_kv_heads=4, dtype="f32", ext_hi=150),
+    "prefix-f32-d64": lambda: _pre(27, head_dim=64, dtype="f32", mode=1, page_size=16,
+                                   pool_slots=8192, n_groups=2, prefix_pages_hi=10, ext_hi=90,
+                                   max_ctx_len=260),
+}
+
+
+# ---------------------------------------------------------------------------
+# rotary table and fused write
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rope_table_matches_oracle(d):
+    say(f"rope_table d={d} max_pos=32768")
+    t = astr.rope_table(32768, d, 10000.0, "cuda")
+    torch.cuda.synchronize()
+    got = t.cpu().numpy().astype(np.float64)
+    want = rope.freqs_cis(32768, d)
+    ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - want) <= ulp)
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg3", "cfg2", "g6-d64", "prefix-f32-d64", "cfg4"])
+def test_rope_kv_write(name):
+    cs = (DECODE.get(name) or PREFILL.get(name))()
+    say(f"rope_kv_write case={name} seed={cs.seed} tokens={cs.n_new}")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    torch.cuda.synchronize()
+    pos = E.new_positions(cs)[:, None]
+    exact_k = rope.rotate(cs.k.astype(np.float64), pos, cs.theta)
+    exact_q = rope.rotate(cs.q.astype(np.float64), pos, cs.theta)
+    loc = torch.from_numpy(st.write_meta["out_cache_loc"].astype(np.int64)).cuda()
+    L = cs.layer_id
+    gk = to_np(st.k_buffer[L].index_select(0, loc))
+    gv = to_np(st.v_buffer[L].index_select(0, loc))
+    gq = to_np(st.q)
+    if cs.dtype == "bf16":
+        E.assert_within_ulp(gk, exact_k, "rotated k")
+        E.assert_within_ulp(gq, exact_q, "rotated q")
+    else:
+        assert np.abs(gk - exact_k).max() <= 1e-5
+        assert np.abs(gq - exact_q).max() <= 1e-5
+    assert np.array_equal(gv, cs.v.astype(np.float64)), "v must be copied bit-exactly"
+    # canary: only history and written slots of the attended layer hold numbers
+    touched = np.zeros(cs.pool_slots, dtype=bool)
+    touched[st.write_meta["out_cache_loc"]] = True
+    table = st.pool.table()
+    for b, r in enumerate(st.reqs):
+        hist = int(cs.seq_lens[b] - cs.new_lens[b])
+        touched[table[r, :hist]] = True
+    for buf in (st.k_buffer, st.v_buffer):
+        finite = (~torch.isnan(buf.float()).all(dim=3).all(dim=2)).cpu().numpy()
+        assert np.array_equal(finite[L], touched), "a slot outside out_cache_loc changed"
+        assert not np.delete(finite, L, axis=0).any(), "another layer changed"
+
+
+def test_rope_kv_write_skips_out_of_range_tokens():
+    cs = _pre(31, batch=2, ext_lo=5, ext_hi=5)
+    say("rope_kv_write out-of-range slots and positions are skipped")
+    st = staging.stage(cs)
+    loc = st.write_cache.out_cache_loc.clone()
+    loc[0] = -1
+    loc[1] = cs.pool_slots                      # one past the end
+    pos = st.positions.clone()
+    pos[2] = st.freqs.shape[0]                  # position outside the table
+    q0 = st.q.clone()
+    astr.rope_kv_write(st.q, st.k, st.v, pos, loc, st.freqs, st.write_cache, 0)
+    torch.cuda.synchronize()
+    finite = (~torch.isnan(st.k_buffer[0].float()).all(dim=2).all(dim=1)).cpu().numpy()
+    good = st.write_meta["out_cache_loc"][3:]
+    assert finite.sum() == len(good) and finite[good].all()
+    assert torch.equal(st.q[:3], q0[:3]), "skipped tokens keep their q"
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(DECODE))
+def test_decode_parity(name):
+    cs = DECODE[name]()
+    say(f"decode case={name} seed={cs.seed} B={cs.batch} Hq={cs.n_heads} Hkv={cs.n_kv_heads} "
+        f"D={cs.head_dim} {cs.dtype} lens={cs.seq_lens.min()}..{cs.seq_lens.max()} C={cs.split_chunk}")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    out = staging.run_decode(st)
+    torch.cuda.synchronize()
+    want = E.expected_decode(cs)
+    got = to_np(out)
+    for b in range(cs.batch):
+        E.assert_close(got[b], want[b], cs.dtype, f"{name} request {b} (L={cs.seq_lens[b]})")
+
+
+def test_decode_split_partials_match_oracle():
+    cs = _dec(41, batch=4, len_lo=100, len_hi=900, split_chunk=128)
+    say("decode split partials chunk=128")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    o_part, lse = astr.decode_workspace(st.attn_cache, cs.n_heads, cs.split_chunk)
+    staging.run_decode(st, o_part=o_part, lse_part=lse)
+    torch.cuda.synchronize()
+    q_rot, k_rot = E.rotated_new(cs)
+    off = E.new_offsets(cs)
+    go, gl = to_np(o_part), to_np(lse)
+    for b in range(cs.batch):
+        K, V = E.request_kv(cs, b, k_rot)
+        wo, wl = A.decode_split(q_rot[off[b + 1] - 1], K, V, 1 / math.sqrt(cs.head_dim), cs.split_chunk)
+        ns = wo.shape[1]
+        E.assert_close(go[b, :, :ns], wo, "bf16", f"o_part request {b}")
+        assert np.abs(gl[b, :, :ns] - wl).max() <= 1e-2
+
+
+def test_decode_zero_length_request_gives_zero():
+    cs = _dec(42, lens=[40, 70], split_chunk=32)
+    say("decode with a zero-length entry")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    kv = st.attn_cache.kv_indptr.clone()
+    kv[1] = kv[0]                                   # entry 0 now has no keys
+    kv[2] = kv[1] + 70
+    c2 = astr.KVCache(**{**st.attn_cache.__dict__, "kv_indptr": kv})
+    out = astr.decode_attn(staging.decode_query(st), c2, cs.layer_id, cs.split_chunk)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[0]) == 0
+    want = E.expected_decode(cs, sample=[1])
+    E.assert_close(to_np(out[1]), want[1], "bf16", "request 1")
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(PREFILL))
+def test_prefill_parity(name):
+    cs = PREFILL[name]()
+    say(f"prefill case={name} seed={cs.seed} B={cs.batch} Hq={cs.n_heads} Hkv={cs.n_kv_heads} "
+        f"D={cs.head_dim} {cs.dtype} ext={cs.new_lens.min()}..{cs.new_lens.max()} "
+        f"prefix<={cs.prefix_lens.max()}")
+    st = staging.stage(cs)
+    assert st.cached == list(cs.prefix_lens), "radix hit must equal the drawn prefix"
+    staging.run_write(st)
+    out = staging.run_prefill(st)
+    torch.cuda.synchronize()
+    want = E.expected_prefill(cs)
+    got = to_np(out)
+    off = E.new_offsets(cs)
+    for b in range(cs.batch):
+        E.assert_close(got[off[b]:off[b + 1]], want[b], cs.dtype, f"{name} request {b}")
+
+
+@pytest.mark.parametrize("name", ["cfg4", "prefix-g6-d64", "prefix-f32-d64"])
+def test_last_prefill_row_equals_decode(name):
+    cs = PREFILL[name]()
+    say(f"prefill last row vs decode, case={name}")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    pre = staging.run_prefill(st)
+    dmeta = st.pool.bind(st.reqs, np.ones(cs.batch, dtype=np.int32), 64)
+    dcache = astr.cache_from_bind(st.k_buffer, st.v_buffer, st.pool.table(), dmeta)
+    last = torch.from_numpy((E.new_offsets(cs)[1:] - 1).astype(np.int64)).cuda()
+    q_last = st.q.index_select(0, last).contiguous()
+    dec = astr.decode_attn(q_last, dcache, cs.layer_id, 128)
+    torch.cuda.synchronize()
+    E.assert_close(to_np(dec), to_np(pre.index_select(0, last)), cs.dtype, "decode vs prefill")
+
+
+# ---------------------------------------------------------------------------
+# the large decode workload at full size, on sampled requests
+# ---------------------------------------------------------------------------
+
+def test_decode_full_size_sampled():
+    cs = make_case(5)
+    free, total = torch.cuda.mem_get_info()
+    say(f"decode full size: B={cs.batch} pool_slots={cs.pool_slots} layers={cs.n_layers} "
+        f"layer_id={cs.layer_id} free={free / 2**30:.0f} GiB")
+    st = staging.stage(cs, canary=True)
+    staging.run_write(st)
+    out = staging.run_decode(st)
+    torch.cuda.synchronize()
+    order = np.argsort(cs.seq_lens)
+    sample = sorted({int(order[0]), int(order[1]), int(order[-1]), int(order[-2]),
+                     *np.random.default_rng(0).choice(cs.batch, 6, replace=False).tolist()})
+    want = E.expected_decode(cs, sample=sample)
+    got = to_np(out)
+    for b in sample:
+        E.assert_close(got[b], want[b], "bf16", f"request {b} (L={cs.seq_lens[b]})")
+    assert torch.isfinite(out.float()).all()
+    other = [l for l in range(cs.n_layers) if l != cs.layer_id][:3]
+    for l in other:
+        assert torch.isnan(st.k_buffer[l, :4096].float()).all()

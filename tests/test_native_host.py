@@ -1,0 +1,223 @@
+"""Host-side checks of libastr.so (CPU only, no device calls).
+
+* the library loads and exports every symbol include/astr.h declares;
+* the C++ page-table builder is bit-exact against the oracle's Python builder
+  (AstrAI docs/guides/inference.md, "KVCache System") on the five workloads
+  and several seeds, including the radix warm-up of the prefix workload;
+* argument validation rejects bad calls before any launch (the kernel
+  wrappers raise rather than fall back: inference.md, "Attention Backend").
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle.pagepool import PagePool as OraclePool, PoolError
+from workloads import make_case
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from paged_gqa_attention_rope_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libastr.so not built")
+    return _lib
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    header = open(os.path.join(ROOT, "include", "astr.h")).read()
+    declared = set(re.findall(r"\b(astr_[a-z_0-9]+)\s*\(", header))
+    assert declared == set(L.EXPORTS)
+    so = ctypes.CDLL(L.LIB_PATH)
+    for name in declared:
+        assert hasattr(so, name), name
+
+
+class _Native:
+    """Adapter so both builders run the same flows."""
+
+    def __init__(self, *a):
+        from paged_gqa_attention_rope_amd import PagePool
+        self.p = PagePool(*a)
+
+    def admit(self, tokens, n):
+        return self.p.admit(tokens, n)
+
+    def extend(self, r, n):
+        self.p.extend(r, n)
+
+    def insert(self, r, tokens, n):
+        self.p.insert(r, tokens, n)
+
+    def release(self, r):
+        self.p.release(r)
+
+    def bind(self, reqs, q_lens, q_tile):
+        return self.p.bind(reqs, q_lens, q_tile)
+
+    def table(self):
+        return self.p.table()
+
+
+class _Oracle(_Native):
+    def __init__(self, *a):
+        self.p = OraclePool(*a)
+
+    def table(self):
+        return self.p.table.copy()
+
+
+def _flow(pool_cls, cs):
+    """Admit, warm and extend the case's requests; return (pool, reqs, cached, meta)."""
+    extra = 4 if cs.group_tokens is not None else 0
+    pp = pool_cls(cs.mode, cs.pool_slots, cs.page_size, cs.max_reqs + extra, cs.max_ctx_len,
+                  cs.page_perm)
+    if cs.group_tokens is not None:
+        for toks in cs.group_tokens:
+            if len(toks) == 0:
+                continue
+            r, c = pp.admit(toks, len(toks))
+            pp.extend(r, len(toks) - c)
+            pp.insert(r, toks, len(toks))
+            pp.release(r)
+    reqs, cached = [], []
+    for b in range(cs.batch):
+        if cs.tokens is not None:
+            r, c = pp.admit(cs.tokens[b], len(cs.tokens[b]))
+        else:
+            r, c = pp.admit(None, 0)
+        pp.extend(r, int(cs.seq_lens[b]) - c)
+        reqs.append(r)
+        cached.append(c)
+    q_lens = cs.new_lens if cs.kind == "prefill" else np.ones(cs.batch, dtype=np.int64)
+    meta = pp.bind(reqs, q_lens, cs.q_tile or 64)
+    return pp, reqs, cached, meta
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("seed_off", [0, 101])
+def test_builder_bit_exact_against_oracle(cid, seed_off):
+    _lib()
+    cs = make_case(cid, None if seed_off == 0 else seed_off + cid)
+    pn, rn, cn, mn = _flow(_Native, cs)
+    po, ro, co, mo = _flow(_Oracle, cs)
+    assert rn == ro and cn == co
+    assert np.array_equal(cn, cs.prefix_lens)
+    assert np.array_equal(pn.table(), po.table())
+    for key in ("req_pool_indices", "seq_lens", "out_cache_loc", "kv_indptr", "qo_indptr",
+                "q_tile_to_batch", "q_tile_to_index"):
+        assert np.array_equal(np.asarray(mn[key]), np.asarray(mo[key])), key
+    assert mn["num_q_tiles"] == mo["num_q_tiles"] and mn["max_len"] == mo["max_len"]
+    if cs.mode == 1:
+        assert pn.p.free_pages() == sum(po.p.free)
+        for page in range(0, cs.pool_slots // cs.page_size, max(1, cs.pool_slots // cs.page_size // 97)):
+            assert pn.p.page_ref(page) == po.p.ref[page]
+
+
+def test_builder_lifecycle_matches_oracle():
+    _lib()
+    rng = np.random.default_rng(7)
+    ps = 4
+    pn, po = _Native(1, ps * 40, ps, 6, 64, None), _Oracle(1, ps * 40, ps, 6, 64, None)
+    base = rng.integers(0, 50, size=64).astype(np.int32)
+    live = []
+    for step in range(60):
+        op = rng.integers(0, 4)
+        if op == 0 or not live:
+            n = int(rng.integers(1, 40))
+            toks = base.copy()
+            toks[rng.integers(0, 64, size=2)] = rng.integers(0, 50, size=2)
+            outs = []
+            for p in (pn, po):
+                try:
+                    r, c = p.admit(toks, n)
+                    p.extend(r, n - c)
+                    outs.append((r, c))
+                except Exception as e:
+                    outs.append(type(getattr(e, "status", None) or getattr(e, "kind", None)).__name__)
+                    if isinstance(e, PoolError) or hasattr(e, "status"):
+                        outs[-1] = "err"
+            assert outs[0] == outs[1], (step, outs)
+            if outs[0] != "err":
+                live.append((outs[0][0], toks, n))
+        elif op == 1:
+            r, toks, n = live.pop(int(rng.integers(0, len(live))))
+            for p in (pn, po):
+                p.insert(r, toks, n)
+                p.release(r)
+        elif op == 2:
+            r, toks, n = live[int(rng.integers(0, len(live)))]
+            for p in (pn, po):
+                p.insert(r, toks, n - 1)
+        else:
+            reqs = [x[0] for x in live]
+            q = [int(rng.integers(0, x[2] + 1)) for x in live]
+            mn, mo = pn.bind(reqs, q, 8), po.bind(reqs, q, 8)
+            for key in ("out_cache_loc", "kv_indptr", "qo_indptr", "q_tile_to_batch"):
+                assert np.array_equal(mn[key], mo[key])
+        assert np.array_equal(pn.table(), po.table()), step
+        assert pn.p.free_pages() == sum(po.p.free)
+
+
+def test_builder_errors():
+    L = _lib()
+    from paged_gqa_attention_rope_amd import AstrArgError, AstrError, PagePool
+    with pytest.raises(AstrArgError):
+        PagePool(1, 100, 16, 2, 10)                       # pool not a multiple of pages
+    with pytest.raises(AstrArgError):
+        PagePool(1, 64, 16, 2, 10, np.array([0, 1, 1, 2]))  # not a permutation
+    pp = PagePool(1, 16 * 4, 16, 2, 200)
+    r, _ = pp.admit()
+    pp.extend(r, 40)
+    before = (pp.table(), pp.free_pages())
+    with pytest.raises(AstrError) as ei:
+        pp.extend(r, 40)
+    assert ei.value.status == L.ASTR_E_NOMEM
+    assert np.array_equal(pp.table(), before[0]) and pp.free_pages() == before[1]
+    with pytest.raises(AstrArgError):
+        pp.extend(r, 500)                                 # past max_ctx_len
+    with pytest.raises(AstrArgError):
+        pp.bind([r], [41])                                # q_len > seq_len
+    with pytest.raises(AstrArgError):
+        pp.release(1)                                     # not live
+    pp.admit()
+    with pytest.raises(AstrError):
+        pp.admit()                                        # no request slot
+
+
+def test_attention_calls_validate_before_launch():
+    """Bad dtype/head_dim/group/layer are rejected with no device involved."""
+    L = _lib()
+    so = L.lib()
+    m = L.KvMeta()
+    m.k_buffer = m.v_buffer = 0x1000                      # never dereferenced: rejected first
+    m.pool_slots, m.n_layers, m.n_kv_heads, m.head_dim, m.kv_dtype = 64, 2, 2, 128, L.ASTR_BF16
+    m.batch, m.max_len = 1, 8
+    cases = [
+        (dict(head_dim=96), L.ASTR_E_UNSUPPORTED),
+        (dict(kv_dtype=7), L.ASTR_E_UNSUPPORTED),
+        (dict(n_kv_heads=3), L.ASTR_E_INVAL),             # 8 heads not a multiple of 3
+        (dict(n_kv_heads=1, n_layers=2), L.ASTR_E_INVAL),  # table missing
+    ]
+    for change, want in cases:
+        mm = L.KvMeta.from_buffer_copy(m)
+        for k, v in change.items():
+            setattr(mm, k, v)
+        st = so.astr_decode_attn(ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), 8,
+                                 ctypes.byref(mm), 0, 64, 0.0, None, None, None)
+        assert st == want, (change, st)
+    st = so.astr_decode_attn(None, None, 8, ctypes.byref(m), 5, 64, 0.0, None, None, None)
+    assert st == L.ASTR_E_INVAL                          # layer out of range
+    st = so.astr_rope_kv_write(None, None, None, None, None, 0, 8, None, 1, ctypes.byref(m), 0, None)
+    assert st == L.ASTR_OK                               # zero tokens: a no-op
+    st = so.astr_rope_table(None, 10, 64, 10000.0, None)
+    assert st == L.ASTR_E_INVAL
+    assert so.astr_decode_num_splits(1000, 256) == 4
+    assert so.astr_decode_num_splits(0, 256) == 1
+    assert so.astr_decode_num_splits(10, 0) == 0
+    assert b"layer" in so.astr_last_error() or b"rope_table" in so.astr_last_error()
