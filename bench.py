@@ -82,6 +82,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (a reference dispatch of "
+                         "known size for calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -130,6 +133,12 @@ def main():
         if ev:
             ev[4].record(stream)
 
+    if args.copy_probe:
+        src = torch.ones(2 ** 28, dtype=torch.float32, device=dev)     # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -11,7 +11,11 @@ AstrAI paper, "Model Architecture" table: theta = 10 000, citing RoFormer,
 whose frequencies are theta^(-2i/d) for i = 0 .. d/2 - 1 over the whole head.
 
 Readings where the pages are silent: the rotation covers the whole head_dim,
-with no scaling; the table is computed in float64 and rounded to float32.
+with no scaling; the table's angles and cos/sin are computed in float64 and
+rounded to float32 (the pages fix the stored table as float32), and the
+method rotates with those stored float32 entries: ``rotate`` is the exact
+rotation (pinned by the invariants), ``rotate_with_table`` the method's
+table lookup plus complex multiply.
 """
 
 import numpy as np
@@ -33,6 +37,30 @@ def freqs_cis(max_pos: int, head_dim: int, theta: float = 10000.0) -> np.ndarray
     """The [max_pos, head_dim/2, 2] table of [cos, sin], float64."""
     a = angles(np.arange(max_pos), head_dim, theta)
     return np.stack([np.cos(a), np.sin(a)], axis=-1)
+
+
+def freqs_cis_f32(max_pos: int, head_dim: int, theta: float = 10000.0) -> np.ndarray:
+    """The table as the method stores it: float32 [cos, sin] (float64 values
+    rounded to nearest float32), returned as float64 holding those values."""
+    return freqs_cis(max_pos, head_dim, theta).astype(np.float32).astype(np.float64)
+
+
+def rotate_with_table(x, positions, table) -> np.ndarray:
+    """The method's rotation: look up [cos, sin] = table[pos, i] and multiply the
+    complex number (x[2i], x[2i+1]) by cos + i sin, in float64.
+
+    With float32 table entries and inputs of at most float32 precision every
+    product is exact in float64, so the result is the exact rotation by the
+    stored table up to one float64 rounding.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    t = np.asarray(table, dtype=np.float64)[np.asarray(positions)]     # [..., D/2, 2]
+    c, s = t[..., 0], t[..., 1]
+    re, im = x[..., 0::2], x[..., 1::2]
+    out = np.empty(np.broadcast_shapes(x.shape, c.shape[:-1] + (x.shape[-1],)), dtype=np.float64)
+    out[..., 0::2] = re * c - im * s
+    out[..., 1::2] = re * s + im * c
+    return out
 
 
 def rotate(x, positions, theta: float = 10000.0) -> np.ndarray:

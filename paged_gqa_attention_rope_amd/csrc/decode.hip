@@ -24,6 +24,7 @@
 // writes the output directly and pass 2 is not launched.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "mfma.hpp"
 
 namespace astr {
 namespace {
@@ -198,6 +199,222 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 pass 1 on the matrix cores.
+//
+// One workgroup (4 waves) per (request, KV head, split); wave w takes the
+// split's 32-key chunks w, w+4, ...  The chunk's K and V head rows are read
+// from HBM as whole rows (D/8 consecutive lanes per 256-byte row, the pattern
+// the memory system serves at streaming rate for this scattered access) with
+// the non-temporal hint, and pass through a per-wave LDS tile that turns them
+// into matrix-core operands.  With the G query heads of the KV head as the 16
+// MFMA columns (unused columns are zero):
+//   S^T[key][head] = K Q^T        A = K read back from the tile (lane: key
+//                                 l%16, d = 32ks + 8(l/16)), B = Q^T kept in
+//                                 registers;
+//   online softmax per head       lane (g, j) holds head j's scores of keys
+//                                 16kb + 4g + r;
+//   O^T[d][head] += V^T P^T       B = P^T straight from the S^T accumulators
+//                                 (reduction slot 8g + r <-> key 4g + r,
+//                                 8g + 4 + r <-> key 16 + 4g + r), A = V^T read
+//                                 from the tile with ds_read_b64_tr_b16.
+// Per key and KV head this costs a 256-byte K row, a 256-byte V row, half an
+// MFMA of each product and a few VALU ops for the softmax -- the VALU work of
+// per-lane dot products and cross-lane reductions disappears.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
+    const uint16_t *__restrict__ q, uint16_t *__restrict__ out, float *__restrict__ o_part,
+    float *__restrict__ lse_part, const uint16_t *__restrict__ k_layer,
+    const uint16_t *__restrict__ v_layer, int64_t pool_slots, int n_kv,
+    const int32_t *__restrict__ req_to_token, int num_reqs, int max_ctx_len,
+    const int32_t *__restrict__ req_pool_indices, const int32_t *__restrict__ kv_indptr,
+    int n_heads, int chunk, int n_splits, float scale_log2) {
+    constexpr int KS = D / 32;          // k-steps of S^T
+    constexpr int DB = D / 16;          // 16-row blocks of O^T
+    constexpr int CK = 32;              // keys per wave chunk
+    constexpr int LDV = D + 8;          // padded LDS row, bf16 elements
+    constexpr int WAVES = 4;
+    static_assert(G <= 16, "query heads per KV head must fit the 16 MFMA columns");
+
+    const int kvh = blockIdx.x % n_kv;
+    const int s = (blockIdx.x / n_kv) % n_splits;
+    const int b = blockIdx.x / (n_kv * n_splits);
+    const int req = req_pool_indices[b];
+    const int L = request_len(kv_indptr, b, req, num_reqs, min(max_ctx_len, n_splits * chunk));
+    const int start = s * chunk;
+    if (start >= L && s > 0) return;
+    const int end = min(start + chunk, L);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 4, j = lane & 15;
+
+    // LDS: one tile per wave (the chunk's K rows, then its V rows), then the
+    // cross-wave merge
+    constexpr int T_BYTES = WAVES * CK * LDV * 2;
+    constexpr int M_BYTES = WAVES * G * (D + 2) * 4;
+    __shared__ __attribute__((aligned(16))) char smem[T_BYTES > M_BYTES ? T_BYTES : M_BYTES];
+    uint16_t *sT = reinterpret_cast<uint16_t *>(smem) + wave * CK * LDV;
+
+    Frag8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks].u = j < G ? *reinterpret_cast<const uint4 *>(
+                               q + (static_cast<int64_t>(b) * n_heads + kvh * G + j) * D + 32 * ks + 8 * g)
+                         : make_uint4(0, 0, 0, 0);
+    }
+    f32x4_t o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+
+    // Loads: D/8 consecutive lanes read one whole head row (256 bytes for
+    // D = 128), 64/(D/8) rows per instruction, with the non-temporal hint (the
+    // rows are read once).  Slots: lane l holds the slot of key c0 + (l % 32),
+    // fetched one chunk ahead, and is shuffled to the lanes loading that row.
+    constexpr int SL = D / 8;           // 16-byte slices per row
+    constexpr int RPI = 64 / SL;        // rows per load instruction
+    constexpr int NI = CK / RPI;        // load instructions per buffer per chunk
+    const int rr = lane / SL, cc = lane % SL;
+    const int32_t *row = req_to_token + static_cast<int64_t>(req) * max_ctx_len;
+    auto slot_of = [&](int c) -> int32_t {
+        const int key = c + (lane & 31);
+        return key < end ? row[key] : -1;
+    };
+    int32_t sl_now = slot_of(start + wave * CK);
+    for (int c0 = start + wave * CK; c0 < end; c0 += WAVES * CK) {
+        const int32_t sl_next = slot_of(c0 + WAVES * CK);
+        uint4 kx[NI], vx[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int64_t slot = __shfl(sl_now, i * RPI + rr, 64);
+            if (slot >= 0 && slot < pool_slots) {
+                const int64_t off = (slot * n_kv + kvh) * D + 8 * cc;
+                kx[i] = load_nt16(k_layer + off);
+                vx[i] = load_nt16(v_layer + off);
+            } else {
+                kx[i] = make_uint4(0, 0, 0, 0);
+                vx[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        // bit k: key c0 + k exists and has a valid slot
+        const uint32_t okmask = static_cast<uint32_t>(
+            __ballot(c0 + (lane & 31) < end && sl_now >= 0 && sl_now < pool_slots) & 0xffffffffull);
+        // K rows -> LDS -> MFMA A-operand layout (lane: key 16kb + j, d = 32ks + 8g)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4 *>(sT + (i * RPI + rr) * LDV + 8 * cc) = kx[i];
+        wave_lds_fence();
+        Frag8 kf[2][KS];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kf[kb][ks].u = *reinterpret_cast<const uint4 *>(sT + (16 * kb + j) * LDV + 32 * ks + 8 * g);
+        }
+        wave_lds_fence();                       // K read out before V overwrites the tile
+#pragma unroll
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4 *>(sT + (i * RPI + rr) * LDV + 8 * cc) = vx[i];
+        f32x4_t sc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sc[kb] = mfma16(kf[kb][ks], qf[ks], sc[kb]);
+        }
+        // online softmax of column j over keys 16kb + 4g + r
+        float mx = m;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int k = 16 * kb + 4 * g + r;
+                const float x = (okmask >> k) & 1u ? sc[kb][r] * scale_log2 : -INFINITY;
+                sc[kb][r] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float alpha = exp2_sub(m, mx);
+        m = mx;
+        float ps = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = exp2_sub(sc[kb][r], mx);
+                sc[kb][r] = p;
+                ps += p;
+            }
+        }
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[db][r] *= alpha;
+        }
+        Frag8 pf;
+        pf.w[0] = pack_bf16x2(sc[0][0], sc[0][1]);
+        pf.w[1] = pack_bf16x2(sc[0][2], sc[0][3]);
+        pf.w[2] = pack_bf16x2(sc[1][0], sc[1][1]);
+        pf.w[3] = pack_bf16x2(sc[1][2], sc[1][3]);
+        wave_lds_fence();                       // V tile written by all lanes of this wave
+        const uint16_t *va = sT + (4 * g + (j >> 2)) * LDV + 4 * (j & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            Frag8 vf;
+            vf.h[0] = lds_read_tr16(va + 16 * db);
+            vf.h[1] = lds_read_tr16(va + 16 * LDV + 16 * db);
+            o[db] = mfma16(vf, pf, o[db]);
+        }
+        wave_lds_fence();                       // reads done before the next chunk's writes
+        sl_now = sl_next;
+    }
+
+    // row sums of each head over the 4 lane groups
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    __syncthreads();                            // V tiles are dead; reuse LDS for the merge
+    float *s_m = reinterpret_cast<float *>(smem);               // [WAVES][G]
+    float *s_l = s_m + WAVES * G;                               // [WAVES][G]
+    float *s_o = s_l + WAVES * G;                               // [WAVES][G][D]
+    if (j < G) {
+        if (g == 0) {
+            s_m[wave * G + j] = m;
+            s_l[wave * G + j] = lsum;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_o[(wave * G + j) * D + 16 * db + 4 * g + r] = o[db][r];
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += 64 * WAVES) {
+        const int h = idx / D, d = idx % D;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) mx = fmaxf(mx, s_m[w * G + h]);
+        float l = 0.f, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float a = exp2_sub(s_m[w * G + h], mx);
+            l += s_l[w * G + h] * a;
+            acc += s_o[(w * G + h) * D + d] * a;
+        }
+        const float res = l > 0.f ? acc / l : 0.f;
+        const int hq = kvh * G + h;
+        if (n_splits == 1) {
+            out[(static_cast<int64_t>(b) * n_heads + hq) * D + d] = static_cast<uint16_t>(f32_to_bf16_bits(res));
+        } else {
+            const int64_t ps = (static_cast<int64_t>(b) * n_heads + hq) * n_splits + s;
+            o_part[ps * D + d] = res;
+            if (d == 0) lse_part[ps] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+        }
+    }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float *__restrict__ o_part, const float *__restrict__ lse_part, T *__restrict__ out,
@@ -217,29 +434,58 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, lse[s]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    // lane u holds the weight of split s0 + u; 8 partial rows in flight per lane
     float acc[PER] = {};
     float wsum = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float w = lse[s] == -INFINITY ? 0.f : __expf(lse[s] - mx);
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+        const int sl = s0 + lane;
+        const float lw = sl < ns ? lse[sl] : -INFINITY;
+        const float w = lw == -INFINITY ? 0.f : __expf(lw - mx);
         wsum += w;
+        const int n = min(64, ns - s0);
+        for (int u0 = 0; u0 < n; u0 += 8) {
+            float v[8][PER], ww[8];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, op[static_cast<int64_t>(s) * D + lane + 64 * j], acc[j]);
+            for (int u = 0; u < 8; ++u) {
+                const int ss = s0 + u0 + u;
+                ww[u] = __shfl(w, u0 + u, 64);
+#pragma unroll
+                for (int jj = 0; jj < PER; ++jj)
+                    v[u][jj] = ss < ns ? op[static_cast<int64_t>(ss) * D + lane + 64 * jj] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+#pragma unroll
+                for (int jj = 0; jj < PER; ++jj) acc[jj] = fmaf(ww[u], v[u][jj], acc[jj]);
+            }
+        }
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
     T *dst = out + static_cast<int64_t>(bh) * D;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) store_scalar<T>(dst + lane + 64 * j, wsum > 0.f ? acc[j] / wsum : 0.f);
+    for (int jj = 0; jj < PER; ++jj) store_scalar<T>(dst + lane + 64 * jj, wsum > 0.f ? acc[jj] / wsum : 0.f);
 }
 
 template <typename T, int D, int G>
 hipError_t launch_decode_typed(const DecodeArgs &a, hipStream_t s) {
     const int n_kv = a.pool.n_kv_heads;
     const int64_t blocks = static_cast<int64_t>(a.batch) * a.n_splits * n_kv;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                       static_cast<const T *>(a.q), static_cast<T *>(a.out), a.o_part, a.lse_part,
-                       static_cast<const T *>(a.pool.k_layer), static_cast<const T *>(a.pool.v_layer),
-                       a.pool.pool_slots, n_kv, a.req_to_token, a.num_reqs, a.max_ctx_len,
-                       a.req_pool_indices, a.kv_indptr, a.n_heads, a.split_chunk, a.n_splits,
-                       a.scale_log2);
+    if constexpr (sizeof(T) == 2) {
+        hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(a.q), static_cast<uint16_t *>(a.out), a.o_part,
+                           a.lse_part, static_cast<const uint16_t *>(a.pool.k_layer),
+                           static_cast<const uint16_t *>(a.pool.v_layer), a.pool.pool_slots, n_kv,
+                           a.req_to_token, a.num_reqs, a.max_ctx_len, a.req_pool_indices, a.kv_indptr,
+                           a.n_heads, a.split_chunk, a.n_splits, a.scale_log2);
+    } else {
+        hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                           s, static_cast<const T *>(a.q), static_cast<T *>(a.out), a.o_part, a.lse_part,
+                           static_cast<const T *>(a.pool.k_layer), static_cast<const T *>(a.pool.v_layer),
+                           a.pool.pool_slots, n_kv, a.req_to_token, a.num_reqs, a.max_ctx_len,
+                           a.req_pool_indices, a.kv_indptr, a.n_heads, a.split_chunk, a.n_splits,
+                           a.scale_log2);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_splits == 1) return e;
     const int64_t mblocks = (static_cast<int64_t>(a.batch) * a.n_heads + 3) / 4;

@@ -68,6 +68,13 @@ template <> __device__ __forceinline__ void store_scalar<bf16_t>(bf16_t *p, floa
     p->bits = static_cast<uint16_t>(f32_to_bf16_bits(x));
 }
 
+// 16-byte global load with the non-temporal hint (data read once: KV rows).
+__device__ __forceinline__ uint4 load_nt16(const void *p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // exp2(x - m) that is exactly 0 for x = -inf (also when m = -inf).
 __device__ __forceinline__ float exp2_sub(float x, float m) {
     return x == -INFINITY ? 0.f : exp2f(x - m);

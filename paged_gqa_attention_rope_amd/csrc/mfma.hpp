@@ -1,0 +1,60 @@
+// gfx950 matrix-core and LDS-transpose helpers (bf16 in, float32 accumulate).
+//
+// v_mfma_f32_16x16x32_bf16, D[i][j] += sum_k A[i][k] B[k][j], lane l of the wave:
+//   A: holds A[l % 16][8*(l/16) + e], e = 0..7
+//   B: holds B[8*(l/16) + e][l % 16], e = 0..7
+//   D: holds D[4*(l/16) + r][l % 16], r = 0..3
+// The reduction index k only pairs A with B, so any fixed relabelling of the
+// 32 k-slots applied to both operands leaves the product unchanged; the
+// kernels use that to make accumulator registers of one product usable as an
+// operand of the next.
+//
+// ds_read_b64_tr_b16: within each group of 16 lanes, with lane j supplying the
+// address of 4 consecutive 16-bit elements in[j][0..3], lane i receives
+// out[i][e] = in[4e + i/4][i % 4].  If lane j points at row (r0 + j/4),
+// column (c0 + 4*(j % 4)) of a row-major bf16 tile M, lane i receives
+// M[r0 + e][c0 + i], e = 0..3: four rows of one column -- the transposed
+// operand slice an MFMA needs, read straight from a row-major tile.
+// (Both layouts were checked on the device with an in-bounds probe.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace astr {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+
+union Frag8 {                    // 8 bf16 = one MFMA A or B operand slice
+    bf16x8_t v;
+    uint4 u;
+    uint2 h[2];
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ f32x4_t mfma16(const Frag8 &a, const Frag8 &b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+// 8-byte transposing LDS read; `p` must be an 8-byte aligned LDS address.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+    const lds_bf16x4 *a = (const lds_bf16x4 *)((const __attribute__((address_space(3))) char *)p);
+    union {
+        bf16x4_t v;
+        uint2 u;
+    } r;
+    r.v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4 *>(a));
+    return r.u;
+}
+
+// Order this wave's LDS writes before its later LDS reads of other lanes'
+// data (LDS operations of one wave complete in issue order; this keeps the
+// compiler from moving them and waits for the writes).
+__device__ __forceinline__ void wave_lds_fence() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+}  // namespace astr

@@ -26,6 +26,7 @@
 //    K/V tiles of 32 keys staged in LDS as float32, online softmax per key.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "mfma.hpp"
 
 namespace astr {
 namespace {
@@ -165,23 +166,6 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
-union Frag8 {                    // 8 bf16 = one MFMA A or B operand slice
-    bf16x8_t v;
-    uint4 u;
-    uint32_t w[4];
-};
-
-// v_mfma_f32_16x16x32_bf16, D[i][j] += sum_k A[i][k] B[k][j]:
-//   A: lane l holds A[l % 16][8*(l/16) .. 8*(l/16)+7]
-//   B: lane l holds B[8*(l/16) .. 8*(l/16)+7][l % 16]
-//   D: lane l holds D[4*(l/16) + r][l % 16], r = 0..3
-__device__ __forceinline__ f32x4_t mfma16(const Frag8 &a, const Frag8 &b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
-}
-
 template <int D, int G>
 struct MfmaCfg {
     static constexpr int TQ = 64;            // query rows per tile

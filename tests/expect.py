@@ -29,12 +29,23 @@ def new_offsets(cs) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(cs.new_lens)]).astype(np.int64)
 
 
+def table(cs) -> np.ndarray:
+    """The float32 cos/sin table the method stores, built by the oracle."""
+    return rope.freqs_cis_f32(cs.max_ctx_len, cs.head_dim, cs.theta)
+
+
+def rotated_exact(cs, tab=None):
+    """(q, k) of the new tokens rotated by the stored table, before rounding."""
+    tab = table(cs) if tab is None else tab
+    pos = new_positions(cs)[:, None]
+    return (rope.rotate_with_table(cs.q.astype(np.float64), pos, tab),
+            rope.rotate_with_table(cs.k.astype(np.float64), pos, tab))
+
+
 def rotated_new(cs):
     """(q, k) of the new tokens rotated at their positions, rounded as stored."""
-    pos = new_positions(cs)[:, None]
-    q = round_store(rope.rotate(cs.q.astype(np.float64), pos, cs.theta), cs.dtype)
-    k = round_store(rope.rotate(cs.k.astype(np.float64), pos, cs.theta), cs.dtype)
-    return q, k
+    q, k = rotated_exact(cs)
+    return round_store(q, cs.dtype), round_store(k, cs.dtype)
 
 
 def request_kv(cs, b: int, k_rot: np.ndarray):

@@ -120,9 +120,7 @@ def test_rope_kv_write(name):
     st = staging.stage(cs)
     staging.run_write(st)
     torch.cuda.synchronize()
-    pos = E.new_positions(cs)[:, None]
-    exact_k = rope.rotate(cs.k.astype(np.float64), pos, cs.theta)
-    exact_q = rope.rotate(cs.q.astype(np.float64), pos, cs.theta)
+    exact_q, exact_k = E.rotated_exact(cs)
     loc = torch.from_numpy(st.write_meta["out_cache_loc"].astype(np.int64)).cuda()
     L = cs.layer_id
     gk = to_np(st.k_buffer[L].index_select(0, loc))

@@ -95,6 +95,26 @@ def test_freqs_table_matches_rotation():
                                rtol=0, atol=1e-12)
 
 
+def test_rotation_by_the_stored_float32_table():
+    # with the float64 table the lookup form equals the exact rotation; with the
+    # float32 table it differs by at most the table's rounding (2^-24 relative
+    # per entry), and the float32 table is the float64 one rounded to nearest
+    d, n = 128, 4096
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((n, 4, d))
+    pos = rng.integers(0, n, size=(n, 1))
+    np.testing.assert_allclose(rope.rotate_with_table(x, pos, rope.freqs_cis(n, d)),
+                               rope.rotate(x, pos), rtol=0, atol=1e-12)
+    t32 = rope.freqs_cis_f32(n, d)
+    t64 = rope.freqs_cis(n, d)
+    assert np.array_equal(t32, t64.astype(np.float32).astype(np.float64))
+    assert np.all(np.abs(t32 - t64) <= np.spacing(np.abs(t64).astype(np.float32)) / 2)
+    err = np.abs(rope.rotate_with_table(x, pos, t32) - rope.rotate(x, pos))
+    bound = 2.0 ** -24 * (np.abs(x[..., 0::2]) + np.abs(x[..., 1::2]))
+    assert np.all(err[..., 0::2] <= bound) and np.all(err[..., 1::2] <= bound)
+    assert err.max() > 0                       # the stored table is not the exact one
+
+
 # -- bf16 -----------------------------------------------------------------------
 
 def test_round_bf16_matches_torch_on_float32_inputs():
