@@ -238,8 +238,9 @@ int astr_pagepool_extend(astr_pagepool *pp, int req_idx, int n_new);
  * new tokens at its last q_lens[b] positions), into caller-owned host arrays:
  *   seq_lens[batch], out_cache_loc[sum q_lens] (qo order), kv_indptr[batch+1],
  *   qo_indptr[batch+1], q_tile_to_batch / q_tile_to_index [tile_capacity]
- *   (tiles of q_tile rows, request-major, ascending; may be NULL when
- *   tile_capacity is 0), *num_q_tiles, *max_len.
+ *   (tiles of q_tile rows listed heaviest first: by decreasing KV extent
+ *   seen by the tile's last row, ties by batch entry then tile index; may be
+ *   NULL when tile_capacity is 0), *num_q_tiles, *max_len.
  * Errors: INVAL (request not live, q_len > seq_len, tile capacity short). */
 int astr_pagepool_bind(astr_pagepool *pp, const int32_t *req_idx, const int32_t *q_lens,
                        int batch, int q_tile, int32_t *seq_lens, int32_t *out_cache_loc,

@@ -24,8 +24,10 @@ requests are served in the order given and positions in increasing order;
 a logical page maps to physical page ``page_perm[logical]`` when a permutation
 is given; slot = physical_page * page_size + pos % page_size; unused table
 entries are -1; a lookup leaves at least one prompt token to compute, so it
-matches at most floor((n_tokens - 1) / page_size) pages; query tiles are
-request-major, ascending, the last one of a request possibly partial;
+matches at most floor((n_tokens - 1) / page_size) pages; query tiles cover
+q_tile rows each, the last one of a request possibly partial, and are listed
+heaviest first (by the KV extent their last row sees; ties by request, then
+tile index -- the pages fix only the tile -> request maps, not their order);
 ``out_cache_loc`` is flat in ``qo_indptr`` order.
 """
 
@@ -162,14 +164,17 @@ class PagePool:
         kv_indptr = [0]
         qo_indptr = [0]
         loc = []
-        t2b, t2i = [], []
+        tiles = []                     # (KV extent of the tile's last row, batch entry, index)
         for b, (r, L, ql) in enumerate(zip(reqs, seq, q_lens)):
             kv_indptr.append(kv_indptr[-1] + L)
             qo_indptr.append(qo_indptr[-1] + ql)
             loc.extend(int(self.table[r, p]) for p in range(L - ql, L))
             for t in range(-(-ql // q_tile)):
-                t2b.append(b)
-                t2i.append(t)
+                tiles.append((L - ql + min((t + 1) * q_tile, ql), b, t))
+        # heaviest tile first; ties keep request order, then tile order
+        tiles.sort(key=lambda x: (-x[0], x[1], x[2]))
+        t2b = [b for _, b, _ in tiles]
+        t2i = [t for _, _, t in tiles]
         i32 = lambda a: np.asarray(a, dtype=np.int32)
         return dict(req_pool_indices=i32(reqs), seq_lens=i32(seq),
                     out_cache_loc=i32(loc), kv_indptr=i32(kv_indptr),

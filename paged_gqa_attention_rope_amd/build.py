@@ -26,6 +26,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 GXX = os.environ.get("CXX", "g++")
 
 HIP_SOURCES = ["rope.hip", "decode.hip", "prefill.hip"]
+# per-source extra flags: the attention kernels never rely on NaN propagation
+# (masking uses -inf, which stays honoured), and without it every fmaxf of a
+# matrix-core result is preceded by a NaN-quieting canonicalisation
+EXTRA = {"prefill.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
 HIP_HOST_SOURCES = ["abi.cpp"]
 HOST_SOURCES = ["pagepool.cpp"]
 
@@ -52,7 +56,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HIP_HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")

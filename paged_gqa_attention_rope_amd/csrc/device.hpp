@@ -25,6 +25,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Two floats to packed bf16 with the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32, round to nearest even): lo in bits 0..15.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // A 16-byte slice of a head row: 8 bf16 or 4 float32 elements.
 template <typename T> struct Vec;
 

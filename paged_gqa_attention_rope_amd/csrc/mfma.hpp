@@ -50,6 +50,17 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
     return r.u;
 }
 
+// Max over the 4 lanes j, j+16, j+32, j+48 (the same MFMA column in the four
+// lane groups).  v_permlane16_swap / v_permlane32_swap applied to (x, x) leave
+// each lane with its own value and that of its partner 16 (32) lanes away,
+// in one of the two results (checked on the device with an in-bounds probe).
+__device__ __forceinline__ float max_over_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Order this wave's LDS writes before its later LDS reads of other lanes'
 // data (LDS operations of one wave complete in issue order; this keeps the
 // compiler from moving them and waits for the writes).

@@ -9,6 +9,7 @@
 // digest of the page's tokens) only to find candidates; a match always
 // compares the stored token tuple exactly, so the digest never decides it.
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <unordered_map>
@@ -249,8 +250,18 @@ extern "C" int astr_pagepool_bind(astr_pagepool *pp, const int32_t *req_idx, con
                           static_cast<long long>(n_tiles), tile_capacity);
     kv_indptr[0] = 0;
     qo_indptr[0] = 0;
-    int mx = 0, t = 0;
+    int mx = 0;
     int64_t w = 0;
+    // query tiles, each with the KV extent its last row sees
+    struct Tile {
+        int32_t extent, b, idx;
+    };
+    std::vector<Tile> tiles;
+    try {
+        tiles.reserve(static_cast<size_t>(n_tiles));
+    } catch (const std::bad_alloc &) {
+        return astr::fail(ASTR_E_NOMEM, "pagepool_bind: host allocation");
+    }
     for (int b = 0; b < batch; ++b) {
         int r = req_idx[b];
         int L = pp->length[r];
@@ -261,11 +272,19 @@ extern "C" int astr_pagepool_bind(astr_pagepool *pp, const int32_t *req_idx, con
         if (L > mx) mx = L;
         const int32_t *row = pp->table.data() + static_cast<size_t>(r) * pp->max_ctx_len;
         for (int pos = L - ql; pos < L; ++pos) out_cache_loc[w++] = row[pos];
-        if (tile_capacity > 0) {
-            for (int i = 0; i * q_tile < ql; ++i, ++t) {
-                q_tile_to_batch[t] = b;
-                q_tile_to_index[t] = i;
-            }
+        for (int i = 0; i * q_tile < ql; ++i) {
+            const int last = (i + 1) * q_tile < ql ? (i + 1) * q_tile : ql;
+            tiles.push_back({L - ql + last, b, i});
+        }
+    }
+    // longest first (ties: request, then tile index), so that an attention
+    // launch can hand out the heaviest tiles first
+    std::stable_sort(tiles.begin(), tiles.end(),
+                     [](const Tile &x, const Tile &y) { return x.extent > y.extent; });
+    if (tile_capacity > 0) {
+        for (size_t t = 0; t < tiles.size(); ++t) {
+            q_tile_to_batch[t] = tiles[t].b;
+            q_tile_to_index[t] = tiles[t].idx;
         }
     }
     *num_q_tiles = static_cast<int>(n_tiles);

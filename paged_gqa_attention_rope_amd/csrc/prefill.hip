@@ -33,6 +33,20 @@ namespace {
 
 // Row range and KV extent of query tile `t`; false when the tile is empty or
 // its metadata is inconsistent (then the tile is skipped).
+// acc *= alpha with each result tied to its own register: on the rarely
+// taken rescale path the accumulators keep their registers, so the branch
+// join needs no copies on the common path.
+__device__ __forceinline__ void scale_in_place(f32x4_t &acc, float alpha) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float x = acc[r];
+        asm volatile("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(alpha));
+        acc[r] = x;
+    }
+}
+
+constexpr int kXcds = 8;        // accelerator dies (XCDs) of an MI355X, each with its own L2
+
 struct TileInfo {
     int b, req, q0, e, L, p, row0, rows, kv_end;
 };
@@ -168,192 +182,298 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
 // ---------------------------------------------------------------------------
 template <int D, int G>
 struct MfmaCfg {
-    static constexpr int TQ = 64;            // query rows per tile
-    static constexpr int RB = 2;             // 16-row blocks per wave (32 rows)
-    static constexpr int WAVES = 2 * G;      // 2 waves per query head
+    static constexpr int TQ = 64;                    // query rows per tile
+    static constexpr int HW = G == 1 ? 1 : 2;        // query heads per wave
+    static constexpr int GROUPS = G / HW;            // head groups: grid z
+    static constexpr int WAVES = 4;                  // 4 row blocks of 16
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int TK = 64;            // keys per LDS tile
-    static constexpr int KB = TK / 16;       // 16-key blocks per tile
-    static constexpr int KS = D / 32;        // k-steps of the QK^T product
-    static constexpr int DB = D / 16;        // 16-wide d blocks of the output
-    static constexpr int LDK = D + 8;        // padded K row (bf16 elements)
-    static constexpr int LDV = TK + 8;       // padded V^T row (bf16 elements)
+    static constexpr int TK = 64;                    // keys per LDS tile
+    static constexpr int KS = D / 32;                // k-steps of the QK^T product
+    static constexpr int DB = D / 16;                // 16-wide d blocks of the output
+    // padded K/V row (bf16 elements): a 32-byte pad puts consecutive rows 8
+    // banks apart, so the 4 rows x 32 bytes a 16-lane group touches in one
+    // transposing read, and the 16 rows of a 128-bit operand read, spread evenly
+    static constexpr int LDK = D + 16;
+    static constexpr int SL = D / 8;                 // 16-byte slices per row
+    static constexpr int NLD = TK * SL / THREADS;    // K (and V) loads per thread per tile
+    static constexpr int BUF = 2 * TK * LDK;         // K + V tile, bf16 elements
+    static_assert(G % HW == 0 && NLD >= 1 && (TK * SL) % THREADS == 0, "tiling");
 };
 
+// One workgroup per (query tile, KV head, head group of HW query heads).
+// Wave w owns query rows 16w .. 16w+15 of the tile for the HW heads, so every K
+// and V operand read from LDS feeds HW matrix-core products, and holds their
+// Q^T operands and O^T accumulators in registers.  K/V tiles of 64 keys are
+// gathered (whole 256-byte rows, non-temporal) into registers one tile ahead
+// and written to the other half of a double-buffered LDS tile; slot indices
+// are fetched two tiles ahead.  Per 32 keys: S^T = K Q^T, online softmax in
+// the log2 domain with the running max raised only when a row's max grows by
+// more than 8 (exact: the same stale max is used for numerator and
+// denominator, and probabilities stay below 2^8), then O^T += V^T P^T with P
+// straight from the accumulators and V^T from the LDS transpose read.
 template <int D, int G>
-__global__ __launch_bounds__((MfmaCfg<D, G>::THREADS)) void prefill_mfma_kernel(
+__global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kernel(
     const uint16_t *__restrict__ q, uint16_t *__restrict__ out, const uint16_t *__restrict__ k_layer,
     const uint16_t *__restrict__ v_layer, int64_t pool_slots, int n_kv,
     const int32_t *__restrict__ req_to_token, int num_reqs, int max_ctx_len,
     const int32_t *__restrict__ req_pool_indices, const int32_t *__restrict__ qo_indptr,
     const int32_t *__restrict__ kv_indptr, const int32_t *__restrict__ q_tile_to_batch,
     const int32_t *__restrict__ q_tile_to_index, int batch, int total_q, int n_heads,
-    float scale_log2) {
+    int num_q_tiles, float scale_log2) {
     using C = MfmaCfg<D, G>;
-    constexpr int TQ = C::TQ, RB = C::RB, TK = C::TK, KB = C::KB, KS = C::KS, DB = C::DB;
-    constexpr int LDK = C::LDK, LDV = C::LDV;
-    constexpr int SL = D / 8;                    // 16-byte slices per K/V row
+    constexpr int TQ = C::TQ, HW = C::HW, TK = C::TK, KS = C::KS, DB = C::DB, LDK = C::LDK;
+    constexpr int SL = C::SL, NLD = C::NLD;
+    constexpr float kLazy = 8.f;                     // log2-domain slack before a rescale
 
+    // Workgroups are handed to the 8 XCDs round-robin (id % 8).  The tiles
+    // arrive heaviest first, so give XCD c the tiles of rank c, c+8, c+16, ...
+    // (every die gets a balanced, heaviest-first share), and keep all KV heads
+    // and head groups of one tile -- which read the same K/V rows -- on the
+    // die that owns the tile, sharing its L2.  The grid is padded to a
+    // multiple of 8 tiles; padding blocks exit at once.
+    const int units_per_tile = n_kv * C::GROUPS;
+    const int xcd = blockIdx.x % kXcds, k_in = blockIdx.x / kXcds;
+    const int tile = kXcds * (k_in / units_per_tile) + xcd;
+    if (tile >= num_q_tiles) return;
+    const int u = k_in % units_per_tile;
+    const int kvh = u / C::GROUPS;
+    const int grp = u % C::GROUPS;
     TileInfo ti;
-    if (!tile_info(blockIdx.x, q_tile_to_batch, q_tile_to_index, qo_indptr, kv_indptr,
+    if (!tile_info(tile, q_tile_to_batch, q_tile_to_index, qo_indptr, kv_indptr,
                    req_pool_indices, batch, num_reqs, max_ctx_len, total_q, TQ, ti))
         return;
-    const int kvh = blockIdx.y;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int h = kvh * G + (wave >> 1);
-    const int wrow0 = (wave & 1) * (16 * RB);    // first tile row of this wave
-    const int ln = lane & 15, lg = lane >> 4;    // MFMA column / lane group
+    const int g = lane >> 4, j = lane & 15;
+    const int r0 = 16 * wave;                        // first tile row of this wave
+    const int h0 = kvh * G + grp * HW;               // first query head of this wave
+    const int qpos0 = ti.p + ti.row0 + r0;           // position of the wave's first row
+    const int qpos = qpos0 + j;                      // position of this lane's row
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[TK * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDV];
-    __shared__ int sOk[TK];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
+    __shared__ uint8_t sOk[2][TK];
 
-    // Q^T operand (B of S^T = K Q^T): lane holds row (ln) of each row block,
-    // d = 32*ks + 8*lg .. +7.  Rows past the tile end read row 0 (results unused).
-    Frag8 qf[RB][KS];
+    // Q^T operands: lane (g, j) holds row r0 + j, d = 32ks + 8g .. +7 of each head
+    Frag8 qf[HW][KS];
+    {
+        int r = r0 + j;
+        if (r >= ti.rows) r = 0;                     // rows past the tile end: results unused
+        const uint16_t *src = q + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h0) * D + 8 * g;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        int r = wrow0 + 16 * rb + ln;
-        if (r >= ti.rows) r = 0;
-        const uint16_t *src = q + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h) * D + 8 * lg;
+        for (int hh = 0; hh < HW; ++hh) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[rb][ks].u = *reinterpret_cast<const uint4 *>(src + 32 * ks);
+            for (int ks = 0; ks < KS; ++ks)
+                qf[hh][ks].u = *reinterpret_cast<const uint4 *>(src + hh * D + 32 * ks);
+        }
     }
-    f32x4_t o[RB][DB];
-    float m[RB], lsum[RB];
+    f32x4_t o[HW][DB], osum[HW];                    // osum: row sums of P (all 4 entries equal)
+    float m[HW];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        m[rb] = -INFINITY;
-        lsum[rb] = 0.f;
+    for (int hh = 0; hh < HW; ++hh) {
+        m[hh] = -INFINITY;
+        osum[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < DB; ++db) o[hh][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    // this wave's last row and the keys it needs
-    const int wrows = min(16 * RB, ti.rows - wrow0);
-    const int w_kv_end = wrows > 0 ? ti.p + ti.row0 + wrow0 + wrows : 0;
+    Frag8 ones;                                      // bf16 1.0 in every reduction slot
+    ones.u = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
 
+    // gather assignment: load i of this thread covers key (tid + THREADS*i) / SL
+    // of the tile, 16-byte slice (tid + THREADS*i) % SL, for both K and V
     const int32_t *trow = req_to_token + static_cast<int64_t>(ti.req) * max_ctx_len;
-    for (int kt = 0; kt < ti.kv_end; kt += TK) {
-        // stage K (row-major) and V^T (transposed) for keys kt .. kt+TK-1
-        for (int sidx = tid; sidx < TK * SL; sidx += C::THREADS) {
-            const int kr = sidx / SL, c = (sidx % SL) * 8;
-            const int j = kt + kr;
-            const int64_t slot = j < ti.kv_end ? trow[j] : -1;
-            const bool ok = slot >= 0 && slot < pool_slots;
-            uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-            if (ok) {
-                kx = *reinterpret_cast<const uint4 *>(k_layer + (slot * n_kv + kvh) * D + c);
-                vx = *reinterpret_cast<const uint4 *>(v_layer + (slot * n_kv + kvh) * D + c);
-            }
-            *reinterpret_cast<uint4 *>(&sK[kr * LDK + c]) = kx;
-            const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
+    // Loads are unconditional (an out-of-range key or slot reads row 0 of the
+    // table or pool instead) so that no branch joins force an early wait on the
+    // prefetch; invalid rows are zeroed when staged and masked by sOk.
+    auto slots_of = [&](int kt, int32_t (&sl)[NLD]) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sVt[(c + 2 * e) * LDV + kr] = static_cast<uint16_t>(vw[e] & 0xffffu);
-                sVt[(c + 2 * e + 1) * LDV + kr] = static_cast<uint16_t>(vw[e] >> 16);
-            }
-            if (c == 0) sOk[kr] = ok;
+        for (int i = 0; i < NLD; ++i) {
+            const int key = kt + (tid + C::THREADS * i) / SL;
+            const int32_t v = trow[min(key, ti.kv_end - 1)];
+            sl[i] = key < ti.kv_end ? v : -1;
         }
-        __syncthreads();
-        if (kt < w_kv_end) {
-            // S^T[key][row] for KB key blocks x RB row blocks
-            f32x4_t s[RB][KB];
+    };
+    const int row_elems = n_kv * D;                  // pool elements per slot
+    auto gather = [&](const int32_t (&sl)[NLD], uint4 (&kx)[NLD], uint4 (&vx)[NLD]) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
+        for (int i = 0; i < NLD; ++i) {
+            const int32_t slot = sl[i] >= 0 && sl[i] < pool_slots ? sl[i] : 0;
+            const int64_t off = static_cast<int64_t>(slot) * row_elems +
+                                (kvh * D + 8 * ((tid + C::THREADS * i) % SL));
+            // cached loads: every tile of the request reads these rows again
+            kx[i] = *reinterpret_cast<const uint4 *>(k_layer + off);
+            vx[i] = *reinterpret_cast<const uint4 *>(v_layer + off);
+        }
+    };
+    auto stage = [&](int buf, const int32_t (&sl)[NLD], const uint4 (&kx)[NLD], const uint4 (&vx)[NLD]) {
+        uint16_t *sK = smem + buf * C::BUF;
+        uint16_t *sV = sK + TK * LDK;
+        bool all_ok = true;
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) s[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NLD; ++i) all_ok = all_ok && sl[i] >= 0 && sl[i] < pool_slots;
+        if (__all(all_ok)) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
+            for (int i = 0; i < NLD; ++i) {
+                const int idx = tid + C::THREADS * i;
+                const int key = idx / SL, c = (idx % SL) * 8;
+                *reinterpret_cast<uint4 *>(sK + key * LDK + c) = kx[i];
+                *reinterpret_cast<uint4 *>(sV + key * LDK + c) = vx[i];
+                if (c == 0) sOk[buf][key] = 1;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int idx = tid + C::THREADS * i;
+                const int key = idx / SL, c = (idx % SL) * 8;
+                const bool ok = sl[i] >= 0 && sl[i] < pool_slots;
+                const uint32_t keep = ok ? 0xffffffffu : 0u;  // value select, no branch
+                uint4 kv = kx[i], vv = vx[i];
+                kv.x &= keep; kv.y &= keep; kv.z &= keep; kv.w &= keep;
+                vv.x &= keep; vv.y &= keep; vv.z &= keep; vv.w &= keep;
+                *reinterpret_cast<uint4 *>(sK + key * LDK + c) = kv;
+                *reinterpret_cast<uint4 *>(sV + key * LDK + c) = vv;
+                if (c == 0) sOk[buf][key] = ok;
+            }
+        }
+    };
+
+    int32_t sl_cur[NLD], sl_nxt[NLD];
+    uint4 kx[NLD], vx[NLD];
+    slots_of(0, sl_cur);
+    slots_of(TK, sl_nxt);
+    gather(sl_cur, kx, vx);
+    stage(0, sl_cur, kx, vx);
+    __syncthreads();
+
+    const int w_last = min(r0 + 15, ti.rows - 1);    // the wave's last valid row
+    const int w_kv_end = w_last >= r0 ? ti.p + ti.row0 + w_last + 1 : 0;
+    for (int kt = 0, it = 0; kt < ti.kv_end; kt += TK, ++it) {
+        const int buf = it & 1;
+        const bool has_next = kt + TK < ti.kv_end;
+        int32_t sl_new[NLD];
+        if (has_next) {
+            // slot indices of tile it+2 first: loads retire in order, so anything
+            // that waits for them must not also wait for the K/V prefetch
+            slots_of(kt + 2 * TK, sl_new);
+            gather(sl_nxt, kx, vx);                  // tile it+1, in flight during compute
+        }
+        const uint64_t okm = __ballot(sOk[buf][lane] != 0);
+        const uint16_t *sK = smem + buf * C::BUF;
+        const uint16_t *sV = sK + TK * LDK;
+#pragma unroll 1   // one register assignment for the accumulators (no rotation copies)
+        for (int sub = 0; sub < TK / 32; ++sub) {
+            const int kb0 = kt + 32 * sub;           // first key of this 32-key step
+            // a step past the wave's last visible key is fully masked below and
+            // adds nothing (no early exit: that would split the accumulators'
+            // live ranges across a branch join)
+            const bool diag = kb0 + 31 > qpos0;
+            f32x4_t sc[HW][2];
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) {
+                sc[hh][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                sc[hh][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
                     Frag8 kf;
-                    kf.u = *reinterpret_cast<const uint4 *>(&sK[(16 * kb + ln) * LDK + 32 * ks + 8 * lg]);
+                    kf.u = *reinterpret_cast<const uint4 *>(sK + (32 * sub + 16 * kb + j) * LDK + 32 * ks + 8 * g);
 #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mfma16(kf, qf[rb][ks], s[rb][kb]);
+                    for (int hh = 0; hh < HW; ++hh) sc[hh][kb] = mfma16(kf, qf[hh][ks], sc[hh][kb]);
                 }
             }
-            // scale, mask, online softmax; lane holds keys 16*kb + 4*lg + r of row ln
-            const bool diag = kt + TK - 1 > ti.p + ti.row0 + wrow0;
+            // keys of this lane: kb0 + 16kb + 4g + r; row: qpos.  Masking is needed
+            // only where the step crosses the causal diagonal or a slot is missing.
+            const uint32_t okw = static_cast<uint32_t>(okm >> (32 * sub));
+            if (diag || okw != 0xffffffffu) {
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const int qi = ti.row0 + wrow0 + 16 * rb + ln;    // request-local query index
-                float mx = m[rb];
+                for (int hh = 0; hh < HW; ++hh) {
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
+                    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int kl = 16 * kb + 4 * lg + r;
-                        float x = s[rb][kb][r] * scale_log2;
-                        if (!sOk[kl] || (diag && kt + kl > ti.p + qi)) x = -INFINITY;
-                        s[rb][kb][r] = x;
-                        mx = fmaxf(mx, x);
+                        for (int r = 0; r < 4; ++r) {
+                            const int k = 16 * kb + 4 * g + r;
+                            if (!((okw >> k) & 1u) || kb0 + k > qpos) sc[hh][kb][r] = -INFINITY;
+                        }
                     }
                 }
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float alpha = exp2_sub(m[rb], mx);
-                m[rb] = mx;
-                float ps = 0.f;
+            }
+            // running max per head; the accumulators are rescaled only when some
+            // row's max grew by more than kLazy (one wave-uniform branch)
+            float mnew[HW];
+            bool need_any = false;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
+            for (int hh = 0; hh < HW; ++hh) {
+                float mxr = fmaxf(fmaxf(fmaxf(sc[hh][0][0], sc[hh][0][1]), fmaxf(sc[hh][0][2], sc[hh][0][3])),
+                                  fmaxf(fmaxf(sc[hh][1][0], sc[hh][1][1]), fmaxf(sc[hh][1][2], sc[hh][1][3])));
+                const float mx = max_over_groups(mxr) * scale_log2;   // scale > 0 keeps the order
+                const bool need = mx > m[hh] + kLazy;
+                mnew[hh] = need ? mx : m[hh];
+                need_any = need_any || need;
+            }
+            if (__builtin_expect(__any(need_any), 0)) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float pv = exp2_sub(s[rb][kb][r], mx);
-                        s[rb][kb][r] = pv;
-                        ps += pv;
-                    }
-                }
-                lsum[rb] = lsum[rb] * alpha + ps;
+                for (int hh = 0; hh < HW; ++hh) {
+                    const float alpha = exp2_sub(m[hh], mnew[hh]);   // 1 where m is unchanged
+                    scale_in_place(osum[hh], alpha);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) o[rb][db][r] *= alpha;
+                    for (int db = 0; db < DB; ++db) scale_in_place(o[hh][db], alpha);
                 }
             }
-            // O^T += V^T P^T; reduction slot 8*lg + r <-> key 32*ks2 + 4*lg + r,
-            // slot 8*lg + 4 + r <-> key 32*ks2 + 16 + 4*lg + r
+            Frag8 pf[HW];
 #pragma unroll
-            for (int ks2 = 0; ks2 < TK / 32; ++ks2) {
-                Frag8 pf[RB];
+            for (int hh = 0; hh < HW; ++hh) {
+                m[hh] = mnew[hh];
+                // exp2 of a masked score (-inf) is 0; the offset is kept finite so
+                // that a row with nothing visible yet cannot form -inf + inf
+                const float neg_m = m[hh] == -INFINITY ? 0.f : -m[hh];
+                float p[2][4];
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    const f32x4_t a = s[rb][2 * ks2], b = s[rb][2 * ks2 + 1];
-                    pf[rb].w[0] = pack_bf16x2(a[0], a[1]);
-                    pf[rb].w[1] = pack_bf16x2(a[2], a[3]);
-                    pf[rb].w[2] = pack_bf16x2(b[0], b[1]);
-                    pf[rb].w[3] = pack_bf16x2(b[2], b[3]);
+                for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        // raw v_exp_f32: results below 2^-126 flush to zero, which is
+                        // immaterial next to the row's maximum term (>= 2^-8)
+                        p[kb][r] = __builtin_amdgcn_exp2f(fmaf(sc[hh][kb][r], scale_log2, neg_m));
                 }
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const uint16_t *vrow = &sVt[(16 * db + ln) * LDV + 32 * ks2 + 4 * lg];
-                    Frag8 vf;
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
-                    const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16);
-                    vf.w[0] = lo.x;
-                    vf.w[1] = lo.y;
-                    vf.w[2] = hi.x;
-                    vf.w[3] = hi.y;
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vf, pf[rb], o[rb][db]);
-                }
+                pf[hh].w[0] = cvt_pk_bf16(p[0][0], p[0][1]);
+                pf[hh].w[1] = cvt_pk_bf16(p[0][2], p[0][3]);
+                pf[hh].w[2] = cvt_pk_bf16(p[1][0], p[1][1]);
+                pf[hh].w[3] = cvt_pk_bf16(p[1][2], p[1][3]);
             }
+            // O^T += V^T P^T; reduction slot 8g + r <-> key 4g + r, 8g + 4 + r <-> key 16 + 4g + r
+            const uint16_t *va = sV + (32 * sub + 4 * g + (j >> 2)) * LDK + 4 * (j & 3);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                Frag8 vf;
+                vf.h[0] = lds_read_tr16(va + 16 * db);
+                vf.h[1] = lds_read_tr16(va + 16 * LDK + 16 * db);
+#pragma unroll
+                for (int hh = 0; hh < HW; ++hh) o[hh][db] = mfma16(vf, pf[hh], o[hh][db]);
+            }
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) osum[hh] = mfma16(ones, pf[hh], osum[hh]);
+        }
+        if (has_next) {
+            stage(buf ^ 1, sl_nxt, kx, vx);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) sl_nxt[i] = sl_new[i];
         }
         __syncthreads();
     }
-    // finish: row sums across the 4 lane groups, normalise, store
+    // finish: normalise by the row sums, store
+    const int r = r0 + j;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        float ls = lsum[rb];
-        ls += __shfl_xor(ls, 16, 64);
-        ls += __shfl_xor(ls, 32, 64);
-        const int r = wrow0 + 16 * rb + ln;
+    for (int hh = 0; hh < HW; ++hh) {
+        const float ls = osum[hh][0];
         if (r >= ti.rows) continue;
         const float inv = ls > 0.f ? 1.f / ls : 0.f;
-        uint16_t *dst = out + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h) * D + 4 * lg;
+        uint16_t *dst = out + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h0 + hh) * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             uint2 w;
-            w.x = pack_bf16x2(o[rb][db][0] * inv, o[rb][db][1] * inv);
-            w.y = pack_bf16x2(o[rb][db][2] * inv, o[rb][db][3] * inv);
+            w.x = cvt_pk_bf16(o[hh][db][0] * inv, o[hh][db][1] * inv);
+            w.y = cvt_pk_bf16(o[hh][db][2] * inv, o[hh][db][3] * inv);
             *reinterpret_cast<uint2 *>(dst + 16 * db) = w;
         }
     }
@@ -373,13 +493,15 @@ hipError_t launch_generic(const PrefillArgs &a, hipStream_t s) {
 template <int D, int G>
 hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
     using C = MfmaCfg<D, G>;
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3(a.num_q_tiles, a.pool.n_kv_heads), dim3(C::THREADS),
+    const int64_t units = static_cast<int64_t>((a.num_q_tiles + kXcds - 1) / kXcds) * kXcds *
+                          a.pool.n_kv_heads * C::GROUPS;
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3(static_cast<unsigned>(units)), dim3(C::THREADS),
                        0, s, static_cast<const uint16_t *>(a.q), static_cast<uint16_t *>(a.out),
                        static_cast<const uint16_t *>(a.pool.k_layer),
                        static_cast<const uint16_t *>(a.pool.v_layer), a.pool.pool_slots,
                        a.pool.n_kv_heads, a.req_to_token, a.num_reqs, a.max_ctx_len, a.req_pool_indices,
                        a.qo_indptr, a.kv_indptr, a.q_tile_to_batch, a.q_tile_to_index, a.batch,
-                       a.total_q, a.n_heads, a.scale_log2);
+                       a.total_q, a.n_heads, a.num_q_tiles, a.scale_log2);
     return hipGetLastError();
 }
 

@@ -58,22 +58,29 @@ def test_paged_slots_and_growth():
     m = pp.bind([r0, r1], [13, 16], q_tile=8)
     assert np.array_equal(m["out_cache_loc"], np.concatenate([pp.table[r0, 20:33], pp.table[r1, :16]]))
     assert np.array_equal(m["qo_indptr"], [0, 13, 29])
+    # KV extents seen by each tile's last row: (0,0) 28, (0,1) 33, (1,0) 8, (1,1) 16
     assert np.array_equal(m["q_tile_to_batch"], [0, 0, 1, 1])
-    assert np.array_equal(m["q_tile_to_index"], [0, 1, 0, 1])
+    assert np.array_equal(m["q_tile_to_index"], [1, 0, 1, 0])
 
 
-def test_tile_map_closed_form():
+def test_tile_maps_cover_every_row_heaviest_first():
     rng = np.random.default_rng(1)
     q = rng.integers(1, 300, size=9)
-    pp = PagePool(0, 9 * 300, 1, 9, 300)
-    for L in q:
-        r, _ = pp.admit(None, int(L))
-        pp.extend(r, int(L))
+    pre = 16 * rng.integers(0, 20, size=9)
+    pp = PagePool(0, 9 * 700, 1, 9, 700)
+    for p, L in zip(pre, q):
+        r, _ = pp.admit(None, 0)
+        pp.extend(r, int(p + L))
     m = pp.bind(list(range(9)), list(q), q_tile=64)
     n = -(-q // 64)
     assert m["num_q_tiles"] == n.sum()
-    assert np.array_equal(m["q_tile_to_batch"], np.repeat(np.arange(9), n))
-    assert np.array_equal(m["q_tile_to_index"], np.concatenate([np.arange(x) for x in n]))
+    pairs = list(zip(m["q_tile_to_batch"].tolist(), m["q_tile_to_index"].tolist()))
+    assert sorted(pairs) == [(b, t) for b in range(9) for t in range(n[b])]
+    ext = [int(pre[b] + min(64 * (t + 1), q[b])) for b, t in pairs]
+    assert all(ext[i] >= ext[i + 1] for i in range(len(ext) - 1))
+    for i in range(len(ext) - 1):
+        if ext[i] == ext[i + 1]:
+            assert pairs[i] < pairs[i + 1]
 
 
 def test_nomem_leaves_state_unchanged():
