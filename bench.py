@@ -50,6 +50,71 @@ def prefill_flops(cs) -> int:
     return 4 * cs.head_dim * cs.n_heads * pairs
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_JSON = os.path.join(PROFILES, "hbm_traffic.json")
+KERNEL_SOURCES = {"decode": "paged_gqa_attention_rope_amd/csrc/decode.hip",
+                  "prefill": "paged_gqa_attention_rope_amd/csrc/prefill.hip"}
+# kernels (name prefixes in the rocprofv3 counter CSV) that make up each call
+CALL_KERNELS = {"decode": ("decode_mfma_kernel<128, 4>", "decode_merge_kernel<astr::bf16_t, 128>"),
+                "prefill": ("prefill_mfma_kernel<128, 4>",)}
+
+
+def _sha(path: str) -> str:
+    import hashlib
+    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(call: str):
+    """HBM bytes per call from the committed counter summary, or None when the
+    kernel source has changed since the counters were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_JSON))[call]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != _sha(KERNEL_SOURCES[call]):
+        return None
+    return int(rec["fetch_bytes"] + rec["write_bytes"])
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    into bytes per call, scaled by what each counter reads for the 1 GiB
+    device copy of the same run (--copy-probe)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    name = r["Kernel_Name"].replace("void astr::(anonymous namespace)::", "")
+                    vals.setdefault(name, []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        v = per_kernel(d, counter)
+        copy = max(v.get("__amd_rocclr_copyBuffer", [0.0]))
+        if copy <= 0:
+            raise SystemExit(f"no copy-probe dispatch in {d}")
+        scale = 2 ** 30 / (copy * 1024.0)          # bytes per counter KiB
+        for call, kernels in CALL_KERNELS.items():
+            rec = out.setdefault(call, {"source_sha": _sha(KERNEL_SOURCES[call]), "kernels": {}})
+            total = 0.0
+            for k in kernels:
+                match = [x for name, x in v.items() if name.startswith(k)]
+                kib = sum(match[0]) / len(match[0]) if match else 0.0
+                rec["kernels"].setdefault(k, {})[counter] = {"kib_per_dispatch": round(kib, 1),
+                                                              "bytes": int(kib * 1024 * scale)}
+                total += kib * 1024 * scale
+            rec["fetch_bytes" if counter == "FETCH_SIZE" else "write_bytes"] = int(total)
+            rec[f"{counter.lower()}_scale"] = round(scale, 5)
+    os.makedirs(PROFILES, exist_ok=True)
+    json.dump(out, open(TRAFFIC_JSON, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(cs, budget_s: float = 15.0):
     """The oracle, as it stands, on a bounded sample of the decode workload."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -85,7 +150,12 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device-to-device copy (a reference dispatch of "
                          "known size for calibrating HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(requests shard across GPUs with no exchange; see the design notes)",
@@ -183,13 +253,15 @@ def main():
             "prefill_cached_prefix": int(cs_p.prefix_lens.sum()),
         },
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode"),
                      "kernel": "decode_attn (split-K pass + merge)",
                      "bytes_per_launch": dbytes, "ms_per_launch": round(float(t_dec), 5)},
         "prefill": {"value": round(pre_tfs, 2), "unit": "TFLOP/s",
                     "roofline": {"bound": "mfma", "achieved": round(pre_tfs, 2),
                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                 "frac": round(pre_tfs / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                                 "frac": round(pre_tfs / BF16_PEAK_TFLOPS, 4),
+                                 "traffic": measured_traffic("prefill"),
                                  "kernel": "prefill_attn", "flops_per_launch": pflops,
                                  "ms_per_launch": round(float(t_pre), 5)}},
         "parts_ms": {"rope_kv_write_decode": round(float(t_wd), 5), "decode_attn": round(float(t_dec), 5),
