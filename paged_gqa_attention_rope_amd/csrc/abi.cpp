@@ -174,6 +174,11 @@ extern "C" int astr_prefill_attn(const void *q, void *out, int total_q, int n_he
         return fail(ASTR_E_INVAL, "prefill_attn: null q, out or tile metadata");
     if (n_heads > 65535) return fail(ASTR_E_UNSUPPORTED, "prefill_attn: too many heads");
     if (total_q < 0) return fail(ASTR_E_INVAL, "prefill_attn: total_q %d", total_q);
+    // bf16: slots wider than a buffer record are addressed as (slot, KV head)
+    // records, whose index must fit 32 bits
+    if (m->kv_dtype == ASTR_BF16 && static_cast<int64_t>(m->n_kv_heads) * m->head_dim * 2 > astr::kMaxRecordStride &&
+        m->pool_slots * m->n_kv_heads > static_cast<int64_t>(UINT32_MAX))
+        return fail(ASTR_E_UNSUPPORTED, "prefill_attn: pool_slots * n_kv_heads exceeds 2^32 - 1");
     a.q = q;
     a.total_q = total_q;
     a.out = out;

@@ -67,6 +67,10 @@ struct PrefillArgs {
     float scale_log2;
 };
 
+// Largest byte stride of a structured-buffer record (14-bit field); the bf16
+// prefill addresses the pool as records of this size or less.
+constexpr int64_t kMaxRecordStride = 16383;
+
 hipError_t launch_rope_table(float *freqs, int max_pos, int head_dim, double theta, hipStream_t s);
 hipError_t launch_rope_kv_write(const RopeArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);

@@ -9,24 +9,25 @@
 // p = L - e positions, query i of the request sits at position p + i.
 //
 // Two kernels:
-//  * prefill_mfma (bf16): one workgroup per (query tile, KV head) holds the
-//    tile's 64 rows for all G query heads of that KV head (2G waves, 32 rows
-//    of one head each), so every K/V tile staged in LDS serves 64*G rows.
-//    QK^T and PV run on the gfx950 bf16 matrix cores
-//    (v_mfma_f32_16x16x32_bf16).  The product is formed transposed,
-//    S^T = K Q^T, so that a lane's accumulator registers hold one query row's
-//    scores for 8 keys -- exactly the B-operand slice the PV product
-//    O^T = V^T P^T needs, with the key order of the reduction chosen to match.
-//    P never leaves registers.  V is stored transposed in LDS for the A
-//    operand; rows are padded by 16 bytes against bank conflicts.  Online
-//    softmax in the log2 domain, fp32 accumulators; P is rounded to bf16 for
-//    the PV product.  Only tiles that cross the causal diagonal are masked.
+//  * prefill_mfma (bf16): one workgroup per (query tile, KV head, pair of query
+//    heads); its 4 waves hold 16 rows x 2 heads each.  Keys stream through a
+//    4-deep LDS ring in steps of 32, filled by asynchronous global->LDS copies
+//    issued 3 steps ahead (slot indices 5 steps ahead), so no register
+//    staging and no wait for memory in the loop.  QK^T and PV run on the
+//    gfx950 bf16 matrix cores (v_mfma_f32_16x16x32_bf16); the product is
+//    formed transposed, S^T = K Q^T, so that a lane's accumulator registers
+//    hold one query row's scores for 8 keys -- exactly the B-operand slice
+//    the PV product O^T = V^T P^T needs.  P never leaves registers; V^T
+//    comes from the LDS transposing read.  Online softmax in the log2 domain
+//    with a lazily raised running max, fp32 accumulators, P rounded to bf16.
 //  * prefill_generic (float32):
 //    one workgroup per (query tile, query head), 4 lanes per query row,
 //    K/V tiles of 32 keys staged in LDS as float32, online softmax per key.
 #include "device.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
+
+#include <type_traits>
 
 namespace astr {
 namespace {
@@ -180,38 +181,128 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
+template <int N>
+using int_c = std::integral_constant<int, N>;
+
 template <int D, int G>
 struct MfmaCfg {
     static constexpr int TQ = 64;                    // query rows per tile
     static constexpr int HW = G == 1 ? 1 : 2;        // query heads per wave
-    static constexpr int GROUPS = G / HW;            // head groups: grid z
+    static constexpr int GROUPS = G / HW;            // head groups per KV head
     static constexpr int WAVES = 4;                  // 4 row blocks of 16
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int TK = 64;                    // keys per LDS tile
+    static constexpr int TS = 32;                    // keys per pipeline step
+    static constexpr int NB = 4;                     // LDS ring depth, in steps
+    static constexpr int AHEAD = NB - 1;             // a step's rows are requested this many steps early
     static constexpr int KS = D / 32;                // k-steps of the QK^T product
     static constexpr int DB = D / 16;                // 16-wide d blocks of the output
-    // padded K/V row (bf16 elements): a 32-byte pad puts consecutive rows 8
-    // banks apart, so the 4 rows x 32 bytes a 16-lane group touches in one
-    // transposing read, and the 16 rows of a 128-bit operand read, spread evenly
-    static constexpr int LDK = D + 16;
-    static constexpr int SL = D / 8;                 // 16-byte slices per row
-    static constexpr int NLD = TK * SL / THREADS;    // K (and V) loads per thread per tile
-    static constexpr int BUF = 2 * TK * LDK;         // K + V tile, bf16 elements
-    static_assert(G % HW == 0 && NLD >= 1 && (TK * SL) % THREADS == 0, "tiling");
+    static constexpr int SL = D / 8;                 // 16-byte chunks per K/V row
+    static constexpr int RB = 2 * D;                 // bytes per K/V row
+    static constexpr int MAT = TS * RB;              // bytes of one step's K (or V) rows
+    static constexpr int RPI = 1024 / RB;            // rows one wave-wide 16-byte copy fills
+    static constexpr int IPW = TS / (RPI * WAVES);   // such copies per wave, step and matrix
+    static_assert(G % HW == 0 && IPW >= 1 && TS % (RPI * WAVES) == 0, "tiling");
 };
+
+// LDS position of 16-byte chunk c of row r of a step's K or V rows: c ^ swz(r).
+// Rows are unpadded (one wave-wide asynchronous copy fills whole rows); the
+// XOR swizzle keeps both the 128-bit K-operand reads (16 rows, one chunk
+// each) and the transposing V reads (4 rows x 32 bytes per 16 lanes) free of
+// LDS bank conflicts (measured with the bank-conflict counter).
+template <int D>
+__device__ __forceinline__ constexpr int swz(int r) {
+    if constexpr (D == 128) {
+        r &= 15;
+        return ((r >> 1) ^ (r << 2)) & 15;
+    } else {
+        return r & 7;
+    }
+}
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding, the
+// other counters unconstrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most N of this wave's asynchronous copies (and other vector
+// memory operations) are outstanding; also a compiler barrier for memory
+// accesses, so no LDS read of copied data moves above it.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that orders LDS traffic without waiting for outstanding
+// global->LDS copies (a full __syncthreads fence would wait for all of them):
+// this wave's LDS reads and writes are complete, then all waves meet.  The
+// copies a step needs are waited for explicitly, by count, before it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8_t *)p));
+}
+
+// Asynchronous global->LDS copies: lane l's 16 (4) bytes land at LDS address
+// lds + 16*l (4*l); lds must be wave-uniform.  Written as inline assembly so
+// that the compiler does not track them: it would otherwise make the LDS
+// reads of other ring slots wait for them.  Their completion is waited for
+// explicitly, by count, before the barrier that publishes the data.  (One
+// wait state separates the M0 write from the copy that reads it.)
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+// 16 bytes at byte `off` of record `idx` of the structured buffer `rsrc`; a
+// record index at or past the buffer's record count reads zeros (the
+// hardware range check).
+__device__ __forceinline__ void copy_record16_to_lds(i32x4_t rsrc, uint32_t idx, uint32_t off, uint32_t lds) {
+    const u32x2_t a = {idx, off};
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 idxen offen lds" ::"v"(a),
+                 "s"(rsrc), "s"(lds)
+                 : "memory", "m0");
+}
+// 4 bytes at byte voff + soff of the raw buffer `rsrc`; bytes past its size read zeros.
+__device__ __forceinline__ void copy_raw4_to_lds(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+                 "s"(soff), "s"(lds)
+                 : "memory", "m0");
+}
+
+// Buffer resource (gfx9 layout) over `records` records of `stride` bytes.
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void *base, uint32_t stride, uint32_t records) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4_t r;
+    r.x = static_cast<int>(static_cast<uint32_t>(a));
+    r.y = static_cast<int>((static_cast<uint32_t>(a >> 32) & 0xffffu) | (stride << 16));
+    r.z = static_cast<int>(records);
+    r.w = 0x00020000;                                // 32-bit data format: raw loads enabled
+    return r;
+}
 
 // One workgroup per (query tile, KV head, head group of HW query heads).
 // Wave w owns query rows 16w .. 16w+15 of the tile for the HW heads, so every K
-// and V operand read from LDS feeds HW matrix-core products, and holds their
-// Q^T operands and O^T accumulators in registers.  K/V tiles of 64 keys are
-// gathered (whole 256-byte rows, non-temporal) into registers one tile ahead
-// and written to the other half of a double-buffered LDS tile; slot indices
-// are fetched two tiles ahead.  Per 32 keys: S^T = K Q^T, online softmax in
-// the log2 domain with the running max raised only when a row's max grows by
-// more than 8 (exact: the same stale max is used for numerator and
-// denominator, and probabilities stay below 2^8), then O^T += V^T P^T with P
-// straight from the accumulators and V^T from the LDS transpose read.
-template <int D, int G>
+// and V operand read from LDS feeds HW matrix-core products; it keeps the
+// Q^T operands and O^T accumulators in registers.
+//
+// Keys are processed in steps of 32 through a ring of 4 LDS slots (K and V
+// rows of one step each), filled by asynchronous global->LDS copies issued 3
+// steps ahead, whose slot indices are fetched one step before that.  Step s:
+//   barrier (the copies of step s+1 have landed, everyone is done with s-1);
+//   S^T(s+1) = K(s+1) Q^T on the matrix cores while P(s) = exp2(S(s) - m)
+//   is formed on the vector ALUs; O^T += V(s)^T P(s)^T while the row maxima
+//   of S(s+1) are formed; mask S(s+1) where it crosses the causal diagonal or
+//   has a missing slot; raise the running max only when a row's max grew by
+//   more than 8 (exact: the same stale max enters numerator and denominator,
+//   and probabilities stay below 2^8); request step s+3's rows.
+// Row sums come from the matrix cores (P^T against a ones operand).
+template <int D, int G, bool WIDE>
 __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kernel(
     const uint16_t *__restrict__ q, uint16_t *__restrict__ out, const uint16_t *__restrict__ k_layer,
     const uint16_t *__restrict__ v_layer, int64_t pool_slots, int n_kv,
@@ -221,8 +312,8 @@ __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kern
     const int32_t *__restrict__ q_tile_to_index, int batch, int total_q, int n_heads,
     int num_q_tiles, float scale_log2) {
     using C = MfmaCfg<D, G>;
-    constexpr int TQ = C::TQ, HW = C::HW, TK = C::TK, KS = C::KS, DB = C::DB, LDK = C::LDK;
-    constexpr int SL = C::SL, NLD = C::NLD;
+    constexpr int TQ = C::TQ, HW = C::HW, KS = C::KS, DB = C::DB, SL = C::SL, RB = C::RB;
+    constexpr int MAT = C::MAT, TS = C::TS, NB = C::NB, AHEAD = C::AHEAD, RPI = C::RPI, IPW = C::IPW;
     constexpr float kLazy = 8.f;                     // log2-domain slack before a rescale
 
     // Workgroups are handed to the 8 XCDs round-robin (id % 8).  The tiles
@@ -243,15 +334,26 @@ __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kern
                    req_pool_indices, batch, num_reqs, max_ctx_len, total_q, TQ, ti))
         return;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, j = lane & 15;
     const int r0 = 16 * wave;                        // first tile row of this wave
     const int h0 = kvh * G + grp * HW;               // first query head of this wave
     const int qpos0 = ti.p + ti.row0 + r0;           // position of the wave's first row
     const int qpos = qpos0 + j;                      // position of this lane's row
+    const int nsteps = (ti.kv_end + TS - 1) / TS;
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
-    __shared__ uint8_t sOk[2][TK];
+    // the ring: slot i holds one step's K rows, then its V rows
+    __shared__ __attribute__((aligned(1024))) uint8_t ring0[2 * MAT], ring1[2 * MAT], ring2[2 * MAT],
+        ring3[2 * MAT];
+    __shared__ uint32_t badf[NB];                    // per step: keys whose slot lies outside the pool
+    auto ring = [&](auto rc) -> uint8_t * {
+        constexpr int R = decltype(rc)::value;
+        if constexpr (R == 0) return ring0;
+        else if constexpr (R == 1) return ring1;
+        else if constexpr (R == 2) return ring2;
+        else return ring3;
+    };
 
     // Q^T operands: lane (g, j) holds row r0 + j, d = 32ks + 8g .. +7 of each head
     Frag8 qf[HW][KS];
@@ -267,10 +369,16 @@ __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kern
         }
     }
     f32x4_t o[HW][DB], osum[HW];                    // osum: row sums of P (all 4 entries equal)
-    float m[HW];
+    // running row max m (log2 domain, scaled), -m as the exponent offset (0
+    // while nothing is visible, so that -inf + inf never forms), and the raw
+    // score above which a lane's scores call for a larger m
+    float m[HW], neg_m[HW], thr[HW];
+    const float inv_scale = 1.f / scale_log2;
 #pragma unroll
     for (int hh = 0; hh < HW; ++hh) {
         m[hh] = -INFINITY;
+        neg_m[hh] = 0.f;
+        thr[hh] = -INFINITY;
         osum[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[hh][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -278,189 +386,320 @@ __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kern
     Frag8 ones;                                      // bf16 1.0 in every reduction slot
     ones.u = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
 
-    // gather assignment: load i of this thread covers key (tid + THREADS*i) / SL
-    // of the tile, 16-byte slice (tid + THREADS*i) % SL, for both K and V
-    const int32_t *trow = req_to_token + static_cast<int64_t>(ti.req) * max_ctx_len;
-    // Loads are unconditional (an out-of-range key or slot reads row 0 of the
-    // table or pool instead) so that no branch joins force an early wait on the
-    // prefetch; invalid rows are zeroed when staged and masked by sOk.
-    auto slots_of = [&](int kt, int32_t (&sl)[NLD]) {
+    // LDS read offsets within a slot.  K operand (key block kb, k-step ks) of
+    // lane (g, j): row 16kb + j, chunk 4ks + g; V^T operand (d block db) via the
+    // transposing read: lane (g, j) points at row 4g + j/4 (+16 for the second
+    // half), elements 16db + 4(j%4) .. +3.  The swizzle only permutes chunks
+    // inside a row and repeats every 16 rows, so both become a per-lane base
+    // XOR a per-block constant.
+    uint32_t kofs[KS], vofs[DB];
+    {
+        const uint32_t kb0 = RB * j + 16 * (g ^ swz<D>(j));
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int key = kt + (tid + C::THREADS * i) / SL;
-            const int32_t v = trow[min(key, ti.kv_end - 1)];
-            sl[i] = key < ti.kv_end ? v : -1;
-        }
-    };
-    const int row_elems = n_kv * D;                  // pool elements per slot
-    auto gather = [&](const int32_t (&sl)[NLD], uint4 (&kx)[NLD], uint4 (&vx)[NLD]) {
+        for (int ks = 0; ks < KS; ++ks) kofs[ks] = kb0 ^ (64 * ks);
+        const int vr = 4 * g + (j >> 2);
+        const uint32_t vb0 = RB * vr + 8 * (j & 1) + 16 * (((j & 3) >> 1) ^ swz<D>(vr));
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int32_t slot = sl[i] >= 0 && sl[i] < pool_slots ? sl[i] : 0;
-            const int64_t off = static_cast<int64_t>(slot) * row_elems +
-                                (kvh * D + 8 * ((tid + C::THREADS * i) % SL));
-            // cached loads: every tile of the request reads these rows again
-            kx[i] = *reinterpret_cast<const uint4 *>(k_layer + off);
-            vx[i] = *reinterpret_cast<const uint4 *>(v_layer + off);
-        }
-    };
-    auto stage = [&](int buf, const int32_t (&sl)[NLD], const uint4 (&kx)[NLD], const uint4 (&vx)[NLD]) {
-        uint16_t *sK = smem + buf * C::BUF;
-        uint16_t *sV = sK + TK * LDK;
-        bool all_ok = true;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) all_ok = all_ok && sl[i] >= 0 && sl[i] < pool_slots;
-        if (__all(all_ok)) {
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const int idx = tid + C::THREADS * i;
-                const int key = idx / SL, c = (idx % SL) * 8;
-                *reinterpret_cast<uint4 *>(sK + key * LDK + c) = kx[i];
-                *reinterpret_cast<uint4 *>(sV + key * LDK + c) = vx[i];
-                if (c == 0) sOk[buf][key] = 1;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const int idx = tid + C::THREADS * i;
-                const int key = idx / SL, c = (idx % SL) * 8;
-                const bool ok = sl[i] >= 0 && sl[i] < pool_slots;
-                const uint32_t keep = ok ? 0xffffffffu : 0u;  // value select, no branch
-                uint4 kv = kx[i], vv = vx[i];
-                kv.x &= keep; kv.y &= keep; kv.z &= keep; kv.w &= keep;
-                vv.x &= keep; vv.y &= keep; vv.z &= keep; vv.w &= keep;
-                *reinterpret_cast<uint4 *>(sK + key * LDK + c) = kv;
-                *reinterpret_cast<uint4 *>(sV + key * LDK + c) = vv;
-                if (c == 0) sOk[buf][key] = ok;
-            }
-        }
-    };
-
-    int32_t sl_cur[NLD], sl_nxt[NLD];
-    uint4 kx[NLD], vx[NLD];
-    slots_of(0, sl_cur);
-    slots_of(TK, sl_nxt);
-    gather(sl_cur, kx, vx);
-    stage(0, sl_cur, kx, vx);
-    __syncthreads();
-
-    const int w_last = min(r0 + 15, ti.rows - 1);    // the wave's last valid row
-    const int w_kv_end = w_last >= r0 ? ti.p + ti.row0 + w_last + 1 : 0;
-    for (int kt = 0, it = 0; kt < ti.kv_end; kt += TK, ++it) {
-        const int buf = it & 1;
-        const bool has_next = kt + TK < ti.kv_end;
-        int32_t sl_new[NLD];
-        if (has_next) {
-            // slot indices of tile it+2 first: loads retire in order, so anything
-            // that waits for them must not also wait for the K/V prefetch
-            slots_of(kt + 2 * TK, sl_new);
-            gather(sl_nxt, kx, vx);                  // tile it+1, in flight during compute
-        }
-        const uint64_t okm = __ballot(sOk[buf][lane] != 0);
-        const uint16_t *sK = smem + buf * C::BUF;
-        const uint16_t *sV = sK + TK * LDK;
-#pragma unroll 1   // one register assignment for the accumulators (no rotation copies)
-        for (int sub = 0; sub < TK / 32; ++sub) {
-            const int kb0 = kt + 32 * sub;           // first key of this 32-key step
-            // a step past the wave's last visible key is fully masked below and
-            // adds nothing (no early exit: that would split the accumulators'
-            // live ranges across a branch join)
-            const bool diag = kb0 + 31 > qpos0;
-            f32x4_t sc[HW][2];
-#pragma unroll
-            for (int hh = 0; hh < HW; ++hh) {
-                sc[hh][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                sc[hh][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    Frag8 kf;
-                    kf.u = *reinterpret_cast<const uint4 *>(sK + (32 * sub + 16 * kb + j) * LDK + 32 * ks + 8 * g);
-#pragma unroll
-                    for (int hh = 0; hh < HW; ++hh) sc[hh][kb] = mfma16(kf, qf[hh][ks], sc[hh][kb]);
-                }
-            }
-            // keys of this lane: kb0 + 16kb + 4g + r; row: qpos.  Masking is needed
-            // only where the step crosses the causal diagonal or a slot is missing.
-            const uint32_t okw = static_cast<uint32_t>(okm >> (32 * sub));
-            if (diag || okw != 0xffffffffu) {
-#pragma unroll
-                for (int hh = 0; hh < HW; ++hh) {
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int k = 16 * kb + 4 * g + r;
-                            if (!((okw >> k) & 1u) || kb0 + k > qpos) sc[hh][kb][r] = -INFINITY;
-                        }
-                    }
-                }
-            }
-            // running max per head; the accumulators are rescaled only when some
-            // row's max grew by more than kLazy (one wave-uniform branch)
-            float mnew[HW];
-            bool need_any = false;
-#pragma unroll
-            for (int hh = 0; hh < HW; ++hh) {
-                float mxr = fmaxf(fmaxf(fmaxf(sc[hh][0][0], sc[hh][0][1]), fmaxf(sc[hh][0][2], sc[hh][0][3])),
-                                  fmaxf(fmaxf(sc[hh][1][0], sc[hh][1][1]), fmaxf(sc[hh][1][2], sc[hh][1][3])));
-                const float mx = max_over_groups(mxr) * scale_log2;   // scale > 0 keeps the order
-                const bool need = mx > m[hh] + kLazy;
-                mnew[hh] = need ? mx : m[hh];
-                need_any = need_any || need;
-            }
-            if (__builtin_expect(__any(need_any), 0)) {
-#pragma unroll
-                for (int hh = 0; hh < HW; ++hh) {
-                    const float alpha = exp2_sub(m[hh], mnew[hh]);   // 1 where m is unchanged
-                    scale_in_place(osum[hh], alpha);
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) scale_in_place(o[hh][db], alpha);
-                }
-            }
-            Frag8 pf[HW];
-#pragma unroll
-            for (int hh = 0; hh < HW; ++hh) {
-                m[hh] = mnew[hh];
-                // exp2 of a masked score (-inf) is 0; the offset is kept finite so
-                // that a row with nothing visible yet cannot form -inf + inf
-                const float neg_m = m[hh] == -INFINITY ? 0.f : -m[hh];
-                float p[2][4];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        // raw v_exp_f32: results below 2^-126 flush to zero, which is
-                        // immaterial next to the row's maximum term (>= 2^-8)
-                        p[kb][r] = __builtin_amdgcn_exp2f(fmaf(sc[hh][kb][r], scale_log2, neg_m));
-                }
-                pf[hh].w[0] = cvt_pk_bf16(p[0][0], p[0][1]);
-                pf[hh].w[1] = cvt_pk_bf16(p[0][2], p[0][3]);
-                pf[hh].w[2] = cvt_pk_bf16(p[1][0], p[1][1]);
-                pf[hh].w[3] = cvt_pk_bf16(p[1][2], p[1][3]);
-            }
-            // O^T += V^T P^T; reduction slot 8g + r <-> key 4g + r, 8g + 4 + r <-> key 16 + 4g + r
-            const uint16_t *va = sV + (32 * sub + 4 * g + (j >> 2)) * LDK + 4 * (j & 3);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                Frag8 vf;
-                vf.h[0] = lds_read_tr16(va + 16 * db);
-                vf.h[1] = lds_read_tr16(va + 16 * LDK + 16 * db);
-#pragma unroll
-                for (int hh = 0; hh < HW; ++hh) o[hh][db] = mfma16(vf, pf[hh], o[hh][db]);
-            }
-#pragma unroll
-            for (int hh = 0; hh < HW; ++hh) osum[hh] = mfma16(ones, pf[hh], osum[hh]);
-        }
-        if (has_next) {
-            stage(buf ^ 1, sl_nxt, kx, vx);
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) sl_nxt[i] = sl_new[i];
-        }
-        __syncthreads();
+        for (int db = 0; db < DB; ++db) vofs[db] = vb0 ^ (32 * db);
     }
+
+    // Copies: copy c (0..IPW-1) of this wave fills step rows RPI*(IPW*wave+c) ..
+    // +RPI-1; lane l writes chunk position l % SL of row RPI*(IPW*wave+c) + l/SL,
+    // so it reads that row's chunk (l % SL) ^ swz(row).
+    const int crow = RPI * IPW * wave + lane / SL;
+    uint32_t ccol[IPW];
+#pragma unroll
+    for (int c = 0; c < IPW; ++c) ccol[c] = (WIDE ? 0 : kvh * RB) + 16 * ((lane % SL) ^ swz<D>(crow + RPI * c));
+    const int32_t *trow = req_to_token + static_cast<int64_t>(ti.req) * max_ctx_len;
+    // The pool as a structured buffer: records are slots (stride n_kv*RB, at
+    // most 16383 bytes), or, for wider slots, (slot, KV head) rows of RB bytes.
+    const uint32_t slot_lim = static_cast<uint32_t>(min(pool_slots, static_cast<int64_t>(INT32_MAX)));
+    const uint32_t stride = WIDE ? RB : static_cast<uint32_t>(n_kv) * RB;
+    const uint32_t records = WIDE ? static_cast<uint32_t>(min(static_cast<int64_t>(slot_lim) * n_kv,
+                                                              static_cast<int64_t>(UINT32_MAX)))
+                                  : slot_lim;
+    const i32x4_t krs = buffer_rsrc(k_layer, stride, records);
+    const i32x4_t vrs = buffer_rsrc(v_layer, stride, records);
+
+    // Slot indices travel the same way as the rows: wave w's 8 rows of step t
+    // (rows 8w .. 8w+7) have their req_to_token entries copied into that
+    // wave's part of a small LDS ring two steps before the rows are requested.
+    // (Keys past the tile's last visible key take the last one's entry: valid
+    // rows, masked by causality.)  All vector-memory operations of the loop are
+    // then asynchronous LDS copies, which retire in order, so the explicit
+    // wait counts below are exact.
+    static_assert(RPI * IPW == 8, "8 rows per wave and step");
+    __shared__ int32_t sidx0[C::WAVES][8], sidx1[C::WAVES][8], sidx2[C::WAVES][8], sidx3[C::WAVES][8];
+    auto sidx = [&](auto rc) -> int32_t * {
+        constexpr int R = decltype(rc)::value;
+        if constexpr (R == 0) return sidx0[wave];
+        else if constexpr (R == 1) return sidx1[wave];
+        else if constexpr (R == 2) return sidx2[wave];
+        else return sidx3[wave];
+    };
+    // the request's table row up to its last visible key; entries past it read 0
+    const i32x4_t trs = buffer_rsrc(trow, 0, 4u * static_cast<uint32_t>(ti.kv_end));
+    const uint32_t idx_voff = 4u * (8 * wave + lane);
+    auto fetch_idx = [&](auto rc, int t) {
+        if (lane < 8) copy_raw4_to_lds(trs, idx_voff, 4u * TS * t, lds_addr(sidx(rc)));
+    };
+    // A key whose slot lies outside the pool, and every key of a step
+    // t >= nsteps (whose rows are never used; copying zeros keeps the number
+    // of copies per step, and so the explicit wait counts, the same on every
+    // path), gets an out-of-range record index: its K and V rows read zeros.
+    auto issue = [&](auto rc, int t) {
+        constexpr int R = decltype(rc)::value;
+        uint8_t *dst = ring(rc);
+        const int32_t *ix = sidx(rc);
+        const int lim = ti.kv_end - TS * t;         // keys of step t at or past this row are not visible
+        int32_t sls[IPW];                            // all indices first: one LDS round trip
+#pragma unroll
+        for (int c = 0; c < IPW; ++c) sls[c] = ix[lane / SL + RPI * c];
+        bool ok[IPW], bad = false;
+#pragma unroll
+        for (int c = 0; c < IPW; ++c) {
+            ok[c] = static_cast<uint32_t>(sls[c]) < slot_lim;
+            bad = bad || !ok[c];
+        }
+        // record index: the slot (past the pool: zeros by the range check), or
+        // (slot, KV head) for wide slots; out of range past the visible keys
+        uint32_t rec[IPW];
+#pragma unroll
+        for (int c = 0; c < IPW; ++c) {
+            if constexpr (WIDE) rec[c] = ok[c] ? static_cast<uint32_t>(sls[c]) * n_kv + kvh : 0xffffffffu;
+            else rec[c] = static_cast<uint32_t>(sls[c]);
+        }
+        if (lim < TS) {                              // the request's last step, or past it
+#pragma unroll
+            for (int c = 0; c < IPW; ++c)
+                if (crow + RPI * c >= lim) rec[c] = 0xffffffffu;
+        }
+#pragma unroll
+        for (int c = 0; c < IPW; ++c) {
+            const uint32_t dk = lds_addr(dst) + RB * RPI * (IPW * wave + c);
+            copy_record16_to_lds(krs, rec[c], ccol[c], dk);
+            copy_record16_to_lds(vrs, rec[c], ccol[c], dk + MAT);
+        }
+        // this wave's 8 rows (8w .. 8w+7) of the step's missing-slot mask
+        uint32_t byte = 0;
+        if (__builtin_expect(__any(bad), 0)) {
+#pragma unroll
+            for (int c = 0; c < IPW; ++c) {
+                const uint64_t b = __ballot(!ok[c]);
+#pragma unroll
+                for (int r = 0; r < RPI; ++r)
+                    if ((b >> (r * SL)) & 1u) byte |= 1u << (RPI * c + r);
+            }
+        }
+        if (lane == 0) reinterpret_cast<uint8_t *>(&badf[R])[wave] = static_cast<uint8_t>(byte);
+    };
+
+    // K operands of a step (key block kb, k-step ks)
+    auto load_k = [&](auto rc, Frag8 (&kf)[KS][2]) {
+        const uint8_t *base = ring(rc);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                kf[ks][kb].u = *reinterpret_cast<const uint4 *>(base + 16 * RB * kb + kofs[ks]);
+        }
+    };
+    // V^T operands of a step (d block db); reduction slot 8g + r <-> key
+    // 4g + r, 8g + 4 + r <-> key 16 + 4g + r
+    auto load_v = [&](auto rc, Frag8 (&vf)[DB]) {
+        const uint8_t *vbase = ring(rc) + MAT;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            vf[db].h[0] = lds_read_tr16(reinterpret_cast<const uint16_t *>(vbase + vofs[db]));
+            vf[db].h[1] = lds_read_tr16(reinterpret_cast<const uint16_t *>(vbase + 16 * RB + vofs[db]));
+        }
+    };
+    // S^T = K Q^T
+    auto qk = [&](const Frag8 (&kf)[KS][2], f32x4_t (&sc)[HW][2]) {
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+            sc[hh][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            sc[hh][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int hh = 0; hh < HW; ++hh) sc[hh][kb] = mfma16(kf[ks][kb], qf[hh][ks], sc[hh][kb]);
+            }
+        }
+    };
+    // P = exp2(S * scale - m) rounded to bf16, as the B operand of the PV product
+    auto probs = [&](const f32x4_t (&sc)[HW][2], Frag8 (&pf)[HW]) {
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+            // exp2 of a masked score (-inf) is 0
+            float p[2][4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    // raw v_exp_f32: results below 2^-126 flush to zero, which is
+                    // immaterial next to the row's maximum term (>= 2^-8)
+                    p[kb][r] = __builtin_amdgcn_exp2f(fmaf(sc[hh][kb][r], scale_log2, neg_m[hh]));
+            }
+            pf[hh].w[0] = cvt_pk_bf16(p[0][0], p[0][1]);
+            pf[hh].w[1] = cvt_pk_bf16(p[0][2], p[0][3]);
+            pf[hh].w[2] = cvt_pk_bf16(p[1][0], p[1][1]);
+            pf[hh].w[3] = cvt_pk_bf16(p[1][2], p[1][3]);
+        }
+    };
+    // O^T += V^T P^T, and the row sums of P
+    auto pv = [&](const Frag8 (&vf)[DB], const Frag8 (&pf)[HW]) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) o[hh][db] = mfma16(vf[db], pf[hh], o[hh][db]);
+        }
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) osum[hh] = mfma16(ones, pf[hh], osum[hh]);
+    };
+    // raw maxima of this lane's 8 scores per head
+    auto local_max = [&](const f32x4_t (&sc)[HW][2], float (&lm)[HW]) {
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh)
+            lm[hh] = fmaxf(fmaxf(fmaxf(sc[hh][0][0], sc[hh][0][1]), fmaxf(sc[hh][0][2], sc[hh][0][3])),
+                           fmaxf(fmaxf(sc[hh][1][0], sc[hh][1][1]), fmaxf(sc[hh][1][2], sc[hh][1][3])));
+    };
+    // keys of this lane: kb0 + 16kb + 4g + r; row: qpos
+    auto apply_mask = [&](f32x4_t (&sc)[HW][2], int kb0, uint32_t okw) {
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int k = 16 * kb + 4 * g + r;
+                    if (!((okw >> k) & 1u) || kb0 + k > qpos) sc[hh][kb][r] = -INFINITY;
+                }
+            }
+        }
+    };
+    // Raise the running max of the rows where a score exceeds it by more than
+    // kLazy.  Each lane tests its own scores against thr; only when some lane
+    // of the wave fires (rarely, after the first steps) are the row maxima
+    // formed across the four lanes of each row -- so the new max is the same
+    // on all of them -- and the accumulators rescaled.
+    auto update_max = [&](const float (&lm)[HW]) {
+        bool fire = false;
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) fire = fire || lm[hh] > thr[hh];
+        if (__builtin_expect(__any(fire), 0)) {
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) {
+                const float mx = max_over_groups(lm[hh]) * scale_log2;   // scale > 0 keeps the order
+                const float mnew = mx > m[hh] + kLazy ? mx : m[hh];
+                const float alpha = exp2_sub(m[hh], mnew);                // 1 where m is unchanged
+                scale_in_place(osum[hh], alpha);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) scale_in_place(o[hh][db], alpha);
+                m[hh] = mnew;
+                neg_m[hh] = mnew == -INFINITY ? 0.f : -mnew;
+                thr[hh] = (mnew + kLazy) * inv_scale;
+            }
+        }
+    };
+    // mask bits of the keys of a step whose slot lies in the pool
+    auto ok_mask = [&](auto rc) -> uint32_t {
+        constexpr int R = decltype(rc)::value;
+        return ~static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(badf[R])));
+    };
+    // mask where step t crosses the causal diagonal or has a missing slot
+    auto mask_step = [&](auto rc, f32x4_t (&sc)[HW][2], int t, float (&lm)[HW]) {
+        const uint32_t okw = ok_mask(rc);
+        const int kb0 = TS * t;
+        if (kb0 + TS - 1 > qpos0 || okw != 0xffffffffu) {
+            apply_mask(sc, kb0, okw);
+            local_max(sc, lm);
+        }
+    };
+
+    // prologue: the steady-state issue sequence of steps -3 .. -1 (indices of
+    // step t+5, then the rows of step t+3; the indices a copy needs must have
+    // landed before they are read,
+    f32x4_t sA[HW][2], sB[HW][2];                   // scores, by step parity
+    // and each wait names the copies issued after the one it needs)
+    fetch_idx(int_c<0>{}, 0);
+    fetch_idx(int_c<1>{}, 1);
+    fetch_idx(int_c<2>{}, 2);
+    wait_copies<2>();                                  // indices of step 0
+    issue(int_c<0>{}, 0);
+    fetch_idx(int_c<3>{}, 3);
+    wait_copies<2 * IPW + 2>();                        // indices of step 1
+    issue(int_c<1>{}, 1);
+    fetch_idx(int_c<0>{}, 4);
+    wait_copies<4 * IPW + 2>();                        // indices of step 2
+    issue(int_c<2>{}, 2);
+    wait_copies<4 * IPW + 2>();                        // rows of step 0
+    lds_barrier();
+    {
+        Frag8 kf[KS][2];
+        load_k(int_c<0>{}, kf);
+        qk(kf, sA);
+    }
+    {
+        float lm[HW];
+        local_max(sA, lm);
+        mask_step(int_c<0>{}, sA, 0, lm);
+        update_max(lm);
+    }
+
+    // one pipeline step; true after the last one
+    auto step = [&](auto rc, int s, f32x4_t (&sc)[HW][2], f32x4_t (&sn)[HW][2]) -> bool {
+        constexpr int R = decltype(rc)::value;
+        constexpr int R1 = (R + 1) % NB, R3 = (R + AHEAD) % NB;
+        // the rows of step s+1 have landed (those of s+2 may still be in flight:
+        // 2*IPW+1 copies were issued after them)
+        wait_copies<2 * IPW + 1>();
+        lds_barrier();
+        const bool more = s + 1 < nsteps;
+        // all LDS operands of the step first (K of step s+1, V of step s), then
+        // S of step s+1 on the matrix cores interleaved with this step's
+        // probabilities on the vector ALUs, then O += V P interleaved with the
+        // lane maxima of S(s+1) (S of the step after the last is unused)
+        Frag8 kf[KS][2], vf[DB], pf[HW];
+        load_k(int_c<R1>{}, kf);
+        load_v(rc, vf);
+        qk(kf, sn);
+        probs(sc, pf);
+        pv(vf, pf);
+        float lm[HW];
+        local_max(sn, lm);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS + 2 * DB, 0);     // LDS reads
+#pragma unroll
+        for (int i = 0; i < 2 * KS * HW; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);               // three VALU
+        }
+#pragma unroll
+        for (int i = 0; i < DB * HW + HW; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+        }
+        if (more) {
+            mask_step(int_c<R1>{}, sn, s + 1, lm);
+            update_max(lm);
+        }
+        // indices of step s+5, then the rows of step s+3 (their indices, copied
+        // two steps ago, landed before this step's barrier)
+        fetch_idx(int_c<(R + 1) % NB>{}, s + AHEAD + 2);
+        issue(int_c<R3>{}, s + AHEAD);
+        return !more;
+    };
+    for (int s = 0;; s += NB) {
+        if (step(int_c<0>{}, s, sA, sB)) break;
+        if (step(int_c<1>{}, s + 1, sB, sA)) break;
+        if (step(int_c<2>{}, s + 2, sA, sB)) break;
+        if (step(int_c<3>{}, s + 3, sB, sA)) break;
+    }
+    wait_copies<0>();                                // no copy outlives the workgroup
+
     // finish: normalise by the row sums, store
     const int r = r0 + j;
 #pragma unroll
@@ -490,12 +729,12 @@ hipError_t launch_generic(const PrefillArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, bool WIDE>
 hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
     using C = MfmaCfg<D, G>;
     const int64_t units = static_cast<int64_t>((a.num_q_tiles + kXcds - 1) / kXcds) * kXcds *
                           a.pool.n_kv_heads * C::GROUPS;
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3(static_cast<unsigned>(units)), dim3(C::THREADS),
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, G, WIDE>), dim3(static_cast<unsigned>(units)), dim3(C::THREADS),
                        0, s, static_cast<const uint16_t *>(a.q), static_cast<uint16_t *>(a.out),
                        static_cast<const uint16_t *>(a.pool.k_layer),
                        static_cast<const uint16_t *>(a.pool.v_layer), a.pool.pool_slots,
@@ -505,16 +744,24 @@ hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool WIDE>
 hipError_t launch_mfma_g(const PrefillArgs &a, hipStream_t s) {
     switch (a.n_heads / a.pool.n_kv_heads) {
-        case 1: return launch_mfma<D, 1>(a, s);
-        case 2: return launch_mfma<D, 2>(a, s);
-        case 4: return launch_mfma<D, 4>(a, s);
-        case 6: return launch_mfma<D, 6>(a, s);
-        case 8: return launch_mfma<D, 8>(a, s);
+        case 1: return launch_mfma<D, 1, WIDE>(a, s);
+        case 2: return launch_mfma<D, 2, WIDE>(a, s);
+        case 4: return launch_mfma<D, 4, WIDE>(a, s);
+        case 6: return launch_mfma<D, 6, WIDE>(a, s);
+        case 8: return launch_mfma<D, 8, WIDE>(a, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+// Slots wider than a buffer record stride can express (16383 bytes) are
+// addressed as (slot, KV head) rows.
+template <int D>
+hipError_t launch_mfma_d(const PrefillArgs &a, hipStream_t s) {
+    return static_cast<int64_t>(a.pool.n_kv_heads) * D * 2 > kMaxRecordStride ? launch_mfma_g<D, true>(a, s)
+                                                                             : launch_mfma_g<D, false>(a, s);
 }
 
 }  // namespace
@@ -522,7 +769,7 @@ hipError_t launch_mfma_g(const PrefillArgs &a, hipStream_t s) {
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
     if (a.num_q_tiles == 0) return hipSuccess;
     if (a.pool.dtype == 1)
-        return a.pool.head_dim == 128 ? launch_mfma_g<128>(a, s) : launch_mfma_g<64>(a, s);
+        return a.pool.head_dim == 128 ? launch_mfma_d<128>(a, s) : launch_mfma_d<64>(a, s);
     return a.pool.head_dim == 128 ? launch_generic<float, 128>(a, s) : launch_generic<float, 64>(a, s);
 }
 

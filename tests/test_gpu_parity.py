@@ -92,6 +92,10 @@ PREFILL = {
                                    pool_slots=16384, n_groups=2, prefix_pages_hi=12, ext_hi=100,
                                    max_ctx_len=300),
     "g2-f32-d128": lambda: _pre(26, n_heads=8, n_kv_heads=4, dtype="f32", ext_hi=150),
+    # 64 KV heads x 128: a slot is wider than a buffer record stride can express
+    "wide-slot-g1-kv64-d128": lambda: _pre(28, batch=3, n_heads=64, n_kv_heads=64, mode=1,
+                                           page_size=16, pool_slots=4096, n_groups=2,
+                                           prefix_pages_hi=6, ext_lo=20, ext_hi=90, max_ctx_len=200),
     "prefix-f32-d64": lambda: _pre(27, head_dim=64, dtype="f32", mode=1, page_size=16,
                                    pool_slots=8192, n_groups=2, prefix_pages_hi=10, ext_hi=90,
                                    max_ctx_len=260),
