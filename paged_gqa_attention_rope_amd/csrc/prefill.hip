@@ -441,7 +441,10 @@ __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kern
     const i32x4_t trs = buffer_rsrc(trow, 0, 4u * static_cast<uint32_t>(ti.kv_end));
     const uint32_t idx_voff = 4u * (8 * wave + lane);
     auto fetch_idx = [&](auto rc, int t) {
-        if (lane < 8) copy_raw4_to_lds(trs, idx_voff, 4u * TS * t, lds_addr(sidx(rc)));
+        // the step offset as a wave-uniform register (the offset field takes no literal)
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(4u * TS * t);
+        asm volatile("" : : "s"(soff));
+        if (lane < 8) copy_raw4_to_lds(trs, idx_voff, soff, lds_addr(sidx(rc)));
     };
     // A key whose slot lies outside the pool, and every key of a step
     // t >= nsteps (whose rows are never used; copying zeros keeps the number
