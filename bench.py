@@ -56,7 +56,7 @@ KERNEL_SOURCES = {"decode": "paged_gqa_attention_rope_amd/csrc/decode.hip",
                   "prefill": "paged_gqa_attention_rope_amd/csrc/prefill.hip"}
 # kernels (name prefixes in the rocprofv3 counter CSV) that make up each call
 CALL_KERNELS = {"decode": ("decode_mfma_kernel<128, 4>", "decode_merge_kernel<astr::bf16_t, 128>"),
-                "prefill": ("prefill_mfma_kernel<128, 4>",)}
+                "prefill": ("prefill_mfma_kernel<128, 4, false>",)}
 
 
 def _sha(path: str) -> str:
@@ -104,7 +104,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
             total = 0.0
             for k in kernels:
                 match = [x for name, x in v.items() if name.startswith(k)]
-                kib = sum(match[0]) / len(match[0]) if match else 0.0
+                if not match:
+                    raise SystemExit(f"no {k} dispatch in {d}")
+                kib = sum(match[0]) / len(match[0])
                 rec["kernels"].setdefault(k, {})[counter] = {"kib_per_dispatch": round(kib, 1),
                                                               "bytes": int(kib * 1024 * scale)}
                 total += kib * 1024 * scale
