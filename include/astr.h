@@ -112,8 +112,10 @@ int astr_rope_table(float *freqs_cis, int max_pos, int head_dim, double theta, v
  * Mathematics": cached keys keep the rotation of their own position;
  * inference.md, "KV Cache").  R rotates each adjacent pair (x[2i], x[2i+1])
  * as the complex product with freqs_cis[pos, i] (inference.md, "Rotary
- * Embedding Backend": view as complex, multiply, view as real).  Arithmetic
- * is float32; bf16 results are rounded to nearest-even.
+ * Embedding Backend": view as complex, multiply, view as real).  The product
+ * is evaluated in float64 from the float32 table entries (so each result is
+ * the correctly rounded rotation by the table) and rounded once to the
+ * storage type; bf16 rounds to nearest-even.
  *   q              device [n_tokens, n_heads, head_dim] kv_dtype, read and written
  *   k, v           device [n_tokens, m->n_kv_heads, head_dim] kv_dtype, read
  *   positions      device [n_tokens] int32, position of each token
@@ -128,6 +130,26 @@ int astr_rope_kv_write(void *q, const void *k, const void *v,
                        const int32_t *positions, const int32_t *out_cache_loc,
                        int n_tokens, int n_heads, const float *freqs_cis, int max_pos,
                        const astr_kv_meta *m, int layer_id, void *stream);
+
+/*
+ * Gradient of the rotation (the backward pass of the rotary embedding used in
+ * training: internals.md, "Rotary Position Embedding (RoPE)" and
+ * inference.md, "Rotary Embedding Backend" keep the complex-multiply path for
+ * autograd).  The rotation by freqs_cis[pos] is linear, so the gradient with
+ * respect to its input is its transpose applied to the gradient of its output:
+ *   grad[t, h, :] <- R(positions[t])^T grad[t, h, :]        (in place)
+ * i.e. each adjacent pair times the complex conjugate of the same table entry
+ * the forward used.  Evaluated in float64 from the float32 entries, rounded
+ * once to dtype (bf16: nearest-even).
+ *   grad       device [n_tokens, n_heads, head_dim] dtype, read and written
+ *   positions  device [n_tokens] int32
+ *   freqs_cis  device [max_pos, head_dim/2, 2] float32 (astr_rope_table)
+ * n_tokens == 0 is a no-op; tokens whose position is outside [0, max_pos) are
+ * left unchanged.  Errors: INVAL, UNSUPPORTED (dtype, head_dim 64/128 only),
+ * LAUNCH.
+ */
+int astr_rope_backward(void *grad, const int32_t *positions, int n_tokens, int n_heads, int head_dim,
+                       const float *freqs_cis, int max_pos, astr_dtype dtype, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Decode attention (one query token per request)                          */

@@ -78,3 +78,22 @@ def rotate(x, positions, theta: float = 10000.0) -> np.ndarray:
     out[..., 0::2] = re * c - im * s
     out[..., 1::2] = re * s + im * c
     return out
+
+
+def rotate_backward_with_table(g, positions, table) -> np.ndarray:
+    """Gradient of ``rotate_with_table`` with respect to its input, given the
+    gradient ``g`` of its output (the backward pass autograd forms for the
+    complex-multiply path the pages keep for training; internals.md, "Rotary
+    Position Embedding (RoPE)").  The forward map of one pair is the matrix
+    [[c, -s], [s, c]]; its gradient is the transpose [[c, s], [-s, c]]
+    applied to g: (ga, gb) -> (ga c + gb s, gb c - ga s), i.e. multiplication
+    by the complex conjugate of the same table entry.
+    """
+    g = np.asarray(g, dtype=np.float64)
+    t = np.asarray(table, dtype=np.float64)[np.asarray(positions)]
+    c, s = t[..., 0], t[..., 1]
+    ga, gb = g[..., 0::2], g[..., 1::2]
+    out = np.empty(np.broadcast_shapes(g.shape, c.shape[:-1] + (g.shape[-1],)), dtype=np.float64)
+    out[..., 0::2] = ga * c + gb * s
+    out[..., 1::2] = gb * c - ga * s
+    return out

@@ -16,7 +16,8 @@ ASTR_BF16 = 1
 
 # every symbol include/astr.h declares
 EXPORTS = (
-    "astr_last_error", "astr_rope_table", "astr_rope_kv_write", "astr_decode_num_splits",
+    "astr_last_error", "astr_rope_table", "astr_rope_kv_write", "astr_rope_backward",
+    "astr_decode_num_splits",
     "astr_decode_attn", "astr_prefill_attn", "astr_pagepool_create", "astr_pagepool_destroy",
     "astr_pagepool_admit", "astr_pagepool_extend", "astr_pagepool_bind", "astr_pagepool_insert",
     "astr_pagepool_release", "astr_pagepool_table", "astr_pagepool_free_pages",
@@ -56,6 +57,7 @@ def lib():
     L.astr_rope_table.argtypes = [c_vp, c_int, c_int, ctypes.c_double, c_vp]
     L.astr_rope_kv_write.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_vp, c_int,
                                      ctypes.POINTER(KvMeta), c_int, c_vp]
+    L.astr_rope_backward.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_vp, c_int, c_int, c_vp]
     L.astr_decode_num_splits.argtypes = [c_int, c_int]
     L.astr_decode_attn.argtypes = [c_vp, c_vp, c_int, ctypes.POINTER(KvMeta), c_int, c_int,
                                    ctypes.c_float, c_vp, c_vp, c_vp]

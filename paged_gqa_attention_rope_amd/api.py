@@ -161,6 +161,22 @@ def rope_kv_write(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: 
     return q
 
 
+def rope_backward(grad: torch.Tensor, positions: torch.Tensor, freqs_cis: torch.Tensor) -> torch.Tensor:
+    """Gradient of the rotation, in place (astr_rope_backward): grad [tokens, heads, head_dim]
+    of the rotated tensor becomes the gradient of the unrotated one."""
+    _need(grad.dim() == 3, "grad must be [tokens, n_heads, head_dim]")
+    _need(grad.dtype in _DTYPES, "grad must be float32 or bfloat16")
+    t, h, d = (int(x) for x in grad.shape)
+    _dev_tensor(grad, "grad", grad.dtype, grad.device)
+    _dev_tensor(positions, "positions", torch.int32, grad.device, t)
+    _dev_tensor(freqs_cis, "freqs_cis", torch.float32, grad.device)
+    _need(freqs_cis.dim() == 3 and tuple(freqs_cis.shape[1:]) == (d // 2, 2),
+          "freqs_cis must be [max_pos, head_dim/2, 2]")
+    check(lib().astr_rope_backward(_vp(grad), _vp(positions), t, h, d, _vp(freqs_cis),
+                                   int(freqs_cis.shape[0]), _DTYPES[grad.dtype], _stream(grad)))
+    return grad
+
+
 def decode_num_splits(max_len: int, split_chunk: int) -> int:
     return int(lib().astr_decode_num_splits(int(max_len), int(split_chunk)))
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 
@@ -119,6 +120,23 @@ extern "C" int astr_rope_kv_write(void *q, const void *k, const void *v, const i
     a.freqs = freqs_cis;
     a.max_pos = max_pos;
     return astr::launched("rope_kv_write", astr::launch_rope_kv_write(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int astr_rope_backward(void *grad, const int32_t *positions, int n_tokens, int n_heads,
+                                  int head_dim, const float *freqs_cis, int max_pos, astr_dtype dtype,
+                                  void *stream) {
+    if (n_tokens < 0 || n_heads < 1) return fail(ASTR_E_INVAL, "rope_backward: n_tokens %d, n_heads %d", n_tokens, n_heads);
+    if (dtype != ASTR_F32 && dtype != ASTR_BF16) return fail(ASTR_E_UNSUPPORTED, "rope_backward: dtype %d", dtype);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(ASTR_E_UNSUPPORTED, "rope_backward: head_dim %d (supported: 64, 128)", head_dim);
+    if (n_tokens == 0) return ASTR_OK;
+    if (!grad || !positions || !freqs_cis || max_pos < 1)
+        return fail(ASTR_E_INVAL, "rope_backward: null argument or max_pos < 1");
+    if (static_cast<int64_t>(n_tokens) * n_heads * head_dim / 4 > static_cast<int64_t>(UINT32_MAX) * 256)
+        return fail(ASTR_E_UNSUPPORTED, "rope_backward: too many elements");
+    return astr::launched("rope_backward",
+                          astr::launch_rope_backward(grad, positions, n_tokens, n_heads, head_dim, dtype,
+                                                     freqs_cis, max_pos, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int astr_decode_num_splits(int max_len, int split_chunk) {

@@ -73,6 +73,8 @@ constexpr int64_t kMaxRecordStride = 16383;
 
 hipError_t launch_rope_table(float *freqs, int max_pos, int head_dim, double theta, hipStream_t s);
 hipError_t launch_rope_kv_write(const RopeArgs &a, hipStream_t s);
+hipError_t launch_rope_backward(void *grad, const int32_t *positions, int n_tokens, int n_heads, int head_dim,
+                                int dtype, const float *freqs, int max_pos, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 

@@ -1,4 +1,4 @@
-// Rotary position embedding fused with the KV-cache write.
+// Rotary position embedding fused with the KV-cache write, and its gradient.
 //
 // AstrAI docs/developer/internals.md, "Rotary Position Embedding (RoPE)" and
 // "KV Cache Mathematics": q and k are rotated by their token's position and
@@ -90,6 +90,51 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(
     y.store(dst);
 }
 
+// Gradient of the rotation, in place: each pair is multiplied by the complex
+// conjugate of the forward table entry (the exact transpose of the forward
+// map), evaluated in float64 and rounded once, as forward.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_backward_kernel(T *__restrict__ grad,
+                                                            const int32_t *__restrict__ positions,
+                                                            int n_tokens, int n_heads,
+                                                            const float2 *__restrict__ tab, int max_pos) {
+    constexpr int E = Vec<T>::N;      // elements per 16-byte slice
+    constexpr int VPR = D / E;        // slices per head row
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gid >= static_cast<int64_t>(n_tokens) * n_heads * VPR) return;
+    const int vi = static_cast<int>(gid % VPR);
+    const int t = static_cast<int>(gid / VPR / n_heads);
+    const int pos = positions[t];
+    if (pos < 0 || pos >= max_pos) return;
+    T *p = grad + (gid / VPR) * D + vi * E;
+    Vec<T> x;
+    x.load(p);
+    float f[E];
+    x.to_float(f);
+    const float2 *cs = tab + static_cast<int64_t>(pos) * (D / 2) + vi * (E / 2);
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+        const float2 c = cs[j];
+        const double a = f[2 * j], b = f[2 * j + 1];
+        f[2 * j] = static_cast<float>(a * c.x + b * static_cast<double>(c.y));
+        f[2 * j + 1] = static_cast<float>(b * c.x - a * static_cast<double>(c.y));
+    }
+    Vec<T> y;
+    y.from_float(f);
+    y.store(p);
+}
+
+template <typename T, int D>
+hipError_t launch_rope_backward_typed(void *grad, const int32_t *positions, int n_tokens, int n_heads,
+                                      const float *freqs, int max_pos, hipStream_t s) {
+    constexpr int VPR = D / Vec<T>::N;
+    const int64_t total = static_cast<int64_t>(n_tokens) * n_heads * VPR;
+    hipLaunchKernelGGL((rope_backward_kernel<T, D>), dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256),
+                       0, s, static_cast<T *>(grad), positions, n_tokens, n_heads,
+                       reinterpret_cast<const float2 *>(freqs), max_pos);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_rope_typed(const RopeArgs &a, hipStream_t s) {
     constexpr int VPR = D / Vec<T>::N;
@@ -112,6 +157,16 @@ hipError_t launch_rope_table(float *freqs, int max_pos, int head_dim, double the
     hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
                        reinterpret_cast<float2 *>(freqs), max_pos, half, theta);
     return hipGetLastError();
+}
+
+hipError_t launch_rope_backward(void *grad, const int32_t *positions, int n_tokens, int n_heads, int head_dim,
+                                int dtype, const float *freqs, int max_pos, hipStream_t s) {
+    const bool bf = dtype == 1;
+    if (head_dim == 128)
+        return bf ? launch_rope_backward_typed<bf16_t, 128>(grad, positions, n_tokens, n_heads, freqs, max_pos, s)
+                  : launch_rope_backward_typed<float, 128>(grad, positions, n_tokens, n_heads, freqs, max_pos, s);
+    return bf ? launch_rope_backward_typed<bf16_t, 64>(grad, positions, n_tokens, n_heads, freqs, max_pos, s)
+              : launch_rope_backward_typed<float, 64>(grad, positions, n_tokens, n_heads, freqs, max_pos, s);
 }
 
 hipError_t launch_rope_kv_write(const RopeArgs &a, hipStream_t s) {

@@ -20,7 +20,7 @@ import staging
 from oracle import attention as A
 from oracle import rope
 from workloads import make_case
-from workloads.gen import decode_case, prefill_case
+from workloads.gen import bf16_storage, decode_case, prefill_case
 
 pytestmark = pytest.mark.gpu
 
@@ -166,6 +166,35 @@ def test_rope_kv_write_skips_out_of_range_tokens():
     good = st.write_meta["out_cache_loc"][3:]
     assert finite.sum() == len(good) and finite[good].all()
     assert torch.equal(st.q[:3], q0[:3]), "skipped tokens keep their q"
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_rope_backward_matches_oracle(dtype, d):
+    # gradient rows of 24 heads at positions spread over a 32k table, plus
+    # out-of-range positions that must leave their rows unchanged
+    say(f"rope_backward dtype={dtype} d={d}")
+    n, h, max_pos = 3000, 24, 32768
+    rng = np.random.default_rng(40 + d)
+    g = rng.standard_normal((n, h, d)).astype(np.float32)
+    if dtype == "bf16":
+        g = bf16_storage(g)
+    pos = rng.integers(0, max_pos, size=n).astype(np.int32)
+    pos[:3] = [-1, max_pos, 0]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    table = astr.rope_table(max_pos, d, 10000.0, "cuda")
+    gt = torch.from_numpy(g).to(tdt).cuda()
+    astr.rope_backward(gt, torch.from_numpy(pos).cuda(), table)
+    torch.cuda.synchronize()
+    got = gt.float().cpu().numpy().astype(np.float64)
+    tab = table.cpu().numpy().astype(np.float64)          # the stored table (pinned above)
+    ok = (pos >= 0) & (pos < max_pos)
+    want = rope.rotate_backward_with_table(g[ok].astype(np.float64), pos[ok][:, None], tab)
+    assert np.array_equal(got[~ok], g[~ok].astype(np.float64)), "out-of-range rows must be unchanged"
+    if dtype == "bf16":
+        E.assert_within_ulp(got[ok], want, "rope gradient")
+    else:
+        ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got[ok] - want) <= ulp), "rope gradient beyond 1 float32 ulp"
 
 
 # ---------------------------------------------------------------------------

@@ -217,7 +217,13 @@ def test_attention_calls_validate_before_launch():
     assert st == L.ASTR_OK                               # zero tokens: a no-op
     st = so.astr_rope_table(None, 10, 64, 10000.0, None)
     assert st == L.ASTR_E_INVAL
+    # rotary gradient: zero tokens is a no-op; shape and type errors come first
+    assert so.astr_rope_backward(None, None, 0, 4, 128, None, 1, L.ASTR_BF16, None) == L.ASTR_OK
+    assert so.astr_rope_backward(None, None, 5, 4, 96, None, 1, L.ASTR_BF16, None) == L.ASTR_E_UNSUPPORTED
+    assert so.astr_rope_backward(None, None, 5, 4, 128, None, 1, 9, None) == L.ASTR_E_UNSUPPORTED
+    assert so.astr_rope_backward(None, None, 5, 4, 128, None, 1, L.ASTR_F32, None) == L.ASTR_E_INVAL
+    assert so.astr_rope_backward(None, None, -1, 4, 128, None, 1, L.ASTR_F32, None) == L.ASTR_E_INVAL
     assert so.astr_decode_num_splits(1000, 256) == 4
     assert so.astr_decode_num_splits(0, 256) == 1
     assert so.astr_decode_num_splits(10, 0) == 0
-    assert b"layer" in so.astr_last_error() or b"rope_table" in so.astr_last_error()
+    assert b"rope_backward: n_tokens -1" in so.astr_last_error()

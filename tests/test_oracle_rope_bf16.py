@@ -115,6 +115,48 @@ def test_rotation_by_the_stored_float32_table():
     assert err.max() > 0                       # the stored table is not the exact one
 
 
+# -- gradient of the rotation -------------------------------------------------------
+
+def test_rotation_gradient_equals_torch_autograd():
+    # the complex-multiply forward differentiated by torch's autograd (float64,
+    # the table entries as complex numbers) gives the oracle's gradient
+    d, n = 128, 64
+    rng = np.random.default_rng(7)
+    table = rope.freqs_cis_f32(4096, d)
+    pos = rng.integers(0, 4096, size=n)
+    x = rng.standard_normal((n, 3, d))
+    g = rng.standard_normal((n, 3, d))
+    xt = torch.tensor(x, requires_grad=True)
+    tt = torch.tensor(table[pos])                                    # [n, d/2, 2]
+    rot = torch.complex(tt[..., 0], tt[..., 1])[:, None, :]          # [n, 1, d/2]
+    y = torch.view_as_real(torch.view_as_complex(xt.reshape(n, 3, d // 2, 2)) * rot).reshape(n, 3, d)
+    y.backward(torch.tensor(g))
+    want = xt.grad.numpy()
+    np.testing.assert_allclose(rope.rotate_with_table(x, pos[:, None], table), y.detach().numpy(),
+                               rtol=0, atol=1e-12)
+    np.testing.assert_allclose(rope.rotate_backward_with_table(g, pos[:, None], table), want,
+                               rtol=0, atol=1e-12)
+
+
+def test_rotation_gradient_is_the_adjoint_and_undoes_the_rotation():
+    # <R x, g> = <x, R^T g>; with the exact float64 table R^T R = I and the
+    # gradient rotation is the rotation by -pos
+    d, n = 64, 500
+    rng = np.random.default_rng(8)
+    table = rope.freqs_cis_f32(1000, d)
+    pos = rng.integers(0, 1000, size=(n, 1))
+    x = rng.standard_normal((n, 2, d))
+    g = rng.standard_normal((n, 2, d))
+    lhs = np.sum(rope.rotate_with_table(x, pos, table) * g)
+    rhs = np.sum(x * rope.rotate_backward_with_table(g, pos, table))
+    assert abs(lhs - rhs) <= 1e-10 * np.sum(np.abs(x) * np.abs(g))
+    exact = rope.freqs_cis(1000, d)
+    back = rope.rotate_backward_with_table(rope.rotate_with_table(x, pos, exact), pos, exact)
+    np.testing.assert_allclose(back, x, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(rope.rotate_backward_with_table(g, pos, exact), rope.rotate(g, -pos),
+                               rtol=0, atol=1e-12)
+
+
 # -- bf16 -----------------------------------------------------------------------
 
 def test_round_bf16_matches_torch_on_float32_inputs():
