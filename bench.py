@@ -142,6 +142,46 @@ def cpu_baseline(cs, budget_s: float = 15.0):
                       f"from the seeded streams), {dt:.1f} s"}
 
 
+def _time_ms(fn, stream, reps: int = 10, warm: int = 2) -> float:
+    """Mean duration of fn() in ms, from HIP events on `stream`."""
+    import torch
+    for _ in range(warm):
+        fn()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(stream)
+    for i in range(reps):
+        fn()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+
+
+def measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream, dbytes,
+                      write_then_decode_ms):
+    """The adjacent rows: the fused decode write on the decode workload, and
+    the rotary gradient on a gradient of the prefill batch's q shape."""
+    import paged_gqa_attention_rope_amd as astr
+    fused_ms = _time_ms(lambda: astr.decode_attn_write(
+        q_unrot, st_d.k, st_d.v, st_d.attn_cache, cs_d.layer_id, st_d.freqs, cs_d.split_chunk,
+        out=out_d, o_part=o_part, lse_part=lse_part), stream)
+    g = st_p.q.clone()
+    t, h, d = (int(x) for x in g.shape)
+    rb_bytes = 2 * g.numel() * g.element_size() + t * (d // 2) * 8    # grad read + written, table rows
+    rb_ms = _time_ms(lambda: astr.rope_backward(g, st_p.positions, st_p.freqs), stream)
+    return {
+        "decode_attn_write": {
+            "workload": cs_d.name, "ms_per_launch": round(fused_ms, 5),
+            "write_then_decode_ms": round(write_then_decode_ms, 5),
+            "achieved_GBps": round(dbytes / (fused_ms * 1e-3) / 1e9, 2),
+            "frac": round(dbytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "rope_backward": {
+            "shape": [t, h, d], "dtype": "bf16", "bytes_per_launch": rb_bytes,
+            "ms_per_launch": round(rb_ms, 5),
+            "achieved_GBps": round(rb_bytes / (rb_ms * 1e-3) / 1e9, 2),
+            "frac": round(rb_bytes / (rb_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +223,7 @@ def main():
     bind_ms = (time.perf_counter() - t0) * 1e3
 
     q_dec = staging.decode_query(st_d)
+    q_unrot = q_dec.clone()                     # the fused decode takes q before rotation
     out_d = torch.empty_like(q_dec)
     import paged_gqa_attention_rope_amd as astr
     o_part, lse_part = astr.decode_workspace(st_d.attn_cache, cs_d.n_heads, cs_d.split_chunk)
@@ -229,6 +270,9 @@ def main():
     dec_gbs = dbytes / (t_dec * 1e-3) / 1e9
     pre_tfs = pflops / (t_pre * 1e-3) / 1e12
 
+    nxt = measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream, dbytes,
+                            float(t_wd + t_dec))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cs_d)
@@ -269,6 +313,7 @@ def main():
         "parts_ms": {"rope_kv_write_decode": round(float(t_wd), 5), "decode_attn": round(float(t_dec), 5),
                      "rope_kv_write_prefill": round(float(t_wp), 5), "prefill_attn": round(float(t_pre), 5),
                      "host_bind_decode": round(bind_ms, 3)},
+        "next": nxt,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -187,6 +187,30 @@ int astr_decode_attn(const void *q, void *out, int n_heads, const astr_kv_meta *
                      int layer_id, int split_chunk, float sm_scale,
                      float *o_part, float *lse_part, void *stream);
 
+/*
+ * The decode step with its rotary write fused in (inference.md, "Attention
+ * Backend": the paged decode op is handed the step's new k and v and writes
+ * them to the cache itself; internals.md, "KV Cache Mathematics": RoPE is
+ * applied before the write).  For each request b with L_b >= 1 the new token
+ * sits at position L_b - 1 in slot req_to_token[req_pool_indices[b], L_b - 1];
+ * this call does, in one launch (plus the merge when S > 1), what
+ * astr_rope_kv_write (positions L_b - 1, that slot) followed by
+ * astr_decode_attn does, with bit-identical results:
+ *   k_buffer[layer, slot] = R(L_b - 1) k_new[b];  v_buffer[layer, slot] = v_new[b]
+ *   out[b, h] = attention of R(L_b - 1) q[b, h] over the request's L_b keys
+ * q is read only (not rotated in place).
+ *   q            device [batch, n_heads, head_dim] bf16, unrotated
+ *   k_new, v_new device [batch, m->n_kv_heads, head_dim] bf16, unrotated k
+ *   freqs_cis    device [max_pos, head_dim/2, 2] float32, max_pos >= m->max_len
+ *   other arguments as astr_decode_attn.
+ * A new-token slot outside the pool is neither written nor attended.
+ * Errors: as astr_decode_attn; UNSUPPORTED for a float32 pool; INVAL for null
+ * k_new/v_new/freqs_cis or max_pos < max_len.
+ */
+int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, void *out, int n_heads,
+                           const astr_kv_meta *m, int layer_id, const float *freqs_cis, int max_pos,
+                           int split_chunk, float sm_scale, float *o_part, float *lse_part, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Prefill attention (ragged batch, causal, optional cached prefix)        */
 /* ------------------------------------------------------------------------ */

@@ -17,7 +17,7 @@ ASTR_BF16 = 1
 # every symbol include/astr.h declares
 EXPORTS = (
     "astr_last_error", "astr_rope_table", "astr_rope_kv_write", "astr_rope_backward",
-    "astr_decode_num_splits",
+    "astr_decode_num_splits", "astr_decode_attn_write",
     "astr_decode_attn", "astr_prefill_attn", "astr_pagepool_create", "astr_pagepool_destroy",
     "astr_pagepool_admit", "astr_pagepool_extend", "astr_pagepool_bind", "astr_pagepool_insert",
     "astr_pagepool_release", "astr_pagepool_table", "astr_pagepool_free_pages",
@@ -61,6 +61,8 @@ def lib():
     L.astr_decode_num_splits.argtypes = [c_int, c_int]
     L.astr_decode_attn.argtypes = [c_vp, c_vp, c_int, ctypes.POINTER(KvMeta), c_int, c_int,
                                    ctypes.c_float, c_vp, c_vp, c_vp]
+    L.astr_decode_attn_write.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, ctypes.POINTER(KvMeta), c_int, c_vp,
+                                         c_int, c_int, ctypes.c_float, c_vp, c_vp, c_vp]
     L.astr_prefill_attn.argtypes = [c_vp, c_vp, c_int, c_int, ctypes.POINTER(KvMeta), c_int,
                                     ctypes.c_float, c_vp]
     L.astr_pagepool_create.argtypes = [ctypes.POINTER(c_vp), c_int, ctypes.c_int64, c_int, c_int,

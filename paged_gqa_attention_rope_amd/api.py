@@ -217,6 +217,41 @@ def decode_attn(q: torch.Tensor, cache: KVCache, layer_id: int, split_chunk: int
     return out
 
 
+def decode_attn_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: KVCache,
+                      layer_id: int, freqs_cis: torch.Tensor, split_chunk: int, sm_scale: float = 0.0,
+                      out: Optional[torch.Tensor] = None, o_part: Optional[torch.Tensor] = None,
+                      lse_part: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode with the rotary write of the new token fused in (astr_decode_attn_write):
+    q [B, H, D] and k_new/v_new [B, Hkv, D] unrotated; the new token sits at position L_b - 1."""
+    m = _meta(cache)
+    kb = cache.k_buffer
+    b, n_kv, d = cache.batch, int(kb.shape[2]), int(kb.shape[3])
+    _need(q.dim() == 3 and q.shape[0] == b and q.shape[2] == d, "q must be [batch, n_heads, head_dim]")
+    h = int(q.shape[1])
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
+        _dev_tensor(t, name, kb.dtype, kb.device)
+    _need(tuple(k_new.shape) == (b, n_kv, d) and tuple(v_new.shape) == (b, n_kv, d),
+          "k_new and v_new must be [batch, n_kv_heads, head_dim]")
+    _dev_tensor(freqs_cis, "freqs_cis", torch.float32, kb.device)
+    _need(freqs_cis.dim() == 3 and tuple(freqs_cis.shape[1:]) == (d // 2, 2),
+          "freqs_cis must be [max_pos, head_dim/2, 2]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor(out, "out", kb.dtype, kb.device, q.numel())
+    s = decode_num_splits(cache.max_len, split_chunk)
+    if s > 1:
+        if o_part is None or lse_part is None:
+            o_part, lse_part = decode_workspace(cache, h, split_chunk)
+        _dev_tensor(o_part, "o_part", torch.float32, kb.device, b * h * s * d)
+        _dev_tensor(lse_part, "lse_part", torch.float32, kb.device, b * h * s)
+    check(lib().astr_decode_attn_write(_vp(q), _vp(k_new), _vp(v_new), _vp(out), h, ctypes.byref(m),
+                                       int(layer_id), _vp(freqs_cis), int(freqs_cis.shape[0]),
+                                       int(split_chunk), float(sm_scale),
+                                       _vp(o_part) if s > 1 else None, _vp(lse_part) if s > 1 else None,
+                                       _stream(q)))
+    return out
+
+
 def prefill_attn(q: torch.Tensor, cache: KVCache, layer_id: int, sm_scale: float = 0.0,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Ragged causal prefill (astr_prefill_attn); q [sum e_b, H, D] rotated, qo order."""

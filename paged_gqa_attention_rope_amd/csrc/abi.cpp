@@ -145,22 +145,27 @@ extern "C" int astr_decode_num_splits(int max_len, int split_chunk) {
     return s < 1 ? 1 : s;
 }
 
-extern "C" int astr_decode_attn(const void *q, void *out, int n_heads, const astr_kv_meta *m,
-                                int layer_id, int split_chunk, float sm_scale, float *o_part,
-                                float *lse_part, void *stream) {
-    astr::DecodeArgs a{};
-    int st = astr::check_pool("decode_attn", m, n_heads, layer_id, a.pool);
+namespace {
+// Shared by the plain and the fused decode call: validation and arguments.
+int decode_args(const char *what, const void *q, void *out, int n_heads, const astr_kv_meta *m,
+                int layer_id, int split_chunk, float sm_scale, float *o_part, float *lse_part,
+                astr::DecodeArgs &a, bool &empty) {
+    empty = false;
+    int st = astr::check_pool(what, m, n_heads, layer_id, a.pool);
     if (st) return st;
-    st = astr::check_table("decode_attn", m);
+    st = astr::check_table(what, m);
     if (st) return st;
-    if (m->batch == 0) return ASTR_OK;
-    if (!q || !out) return fail(ASTR_E_INVAL, "decode_attn: null q or out");
-    if (split_chunk < 1) return fail(ASTR_E_INVAL, "decode_attn: split_chunk %d", split_chunk);
+    if (m->batch == 0) {
+        empty = true;
+        return ASTR_OK;
+    }
+    if (!q || !out) return fail(ASTR_E_INVAL, "%s: null q or out", what);
+    if (split_chunk < 1) return fail(ASTR_E_INVAL, "%s: split_chunk %d", what, split_chunk);
     const int ns = astr_decode_num_splits(m->max_len, split_chunk);
     if (ns > 1 && (!o_part || !lse_part))
-        return fail(ASTR_E_INVAL, "decode_attn: %d splits need o_part and lse_part", ns);
+        return fail(ASTR_E_INVAL, "%s: %d splits need o_part and lse_part", what, ns);
     if (static_cast<int64_t>(m->batch) * ns * m->n_kv_heads > INT32_MAX)
-        return fail(ASTR_E_UNSUPPORTED, "decode_attn: grid too large");
+        return fail(ASTR_E_UNSUPPORTED, "%s: grid too large", what);
     a.q = q;
     a.out = out;
     a.o_part = o_part;
@@ -175,7 +180,40 @@ extern "C" int astr_decode_attn(const void *q, void *out, int n_heads, const ast
     a.split_chunk = split_chunk;
     a.n_splits = ns;
     a.scale_log2 = astr::scale_of(sm_scale, m->head_dim);
+    return ASTR_OK;
+}
+}  // namespace
+
+extern "C" int astr_decode_attn(const void *q, void *out, int n_heads, const astr_kv_meta *m,
+                                int layer_id, int split_chunk, float sm_scale, float *o_part,
+                                float *lse_part, void *stream) {
+    astr::DecodeArgs a{};
+    bool empty;
+    const int st = decode_args("decode_attn", q, out, n_heads, m, layer_id, split_chunk, sm_scale, o_part,
+                               lse_part, a, empty);
+    if (st || empty) return st;
     return astr::launched("decode_attn", astr::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, void *out,
+                                      int n_heads, const astr_kv_meta *m, int layer_id,
+                                      const float *freqs_cis, int max_pos, int split_chunk, float sm_scale,
+                                      float *o_part, float *lse_part, void *stream) {
+    astr::DecodeArgs a{};
+    bool empty;
+    const int st = decode_args("decode_attn_write", q, out, n_heads, m, layer_id, split_chunk, sm_scale,
+                               o_part, lse_part, a, empty);
+    if (st || empty) return st;
+    if (m->kv_dtype != ASTR_BF16)
+        return fail(ASTR_E_UNSUPPORTED, "decode_attn_write: bf16 only (use astr_rope_kv_write + astr_decode_attn)");
+    if (!k_new || !v_new || !freqs_cis) return fail(ASTR_E_INVAL, "decode_attn_write: null k_new, v_new or freqs_cis");
+    if (max_pos < m->max_len)
+        return fail(ASTR_E_INVAL, "decode_attn_write: max_pos %d < max_len %d", max_pos, m->max_len);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.freqs = freqs_cis;
+    a.max_pos = max_pos;
+    return astr::launched("decode_attn_write", astr::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int astr_prefill_attn(const void *q, void *out, int total_q, int n_heads,

@@ -221,15 +221,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 // Per key and KV head this costs a 256-byte K row, a 256-byte V row, half an
 // MFMA of each product and a few VALU ops for the softmax -- the VALU work of
 // per-lane dot products and cross-lane reductions disappears.
+//
+// FUSED: the step's new token is rotated and written here (inference.md,
+// "Attention Backend": the decode op takes the new k/v and writes them to the
+// cache).  q arrives unrotated and every workgroup rotates its G heads at
+// position L_b - 1; the workgroup whose split holds key L_b - 1 rotates
+// k_new, uses it and v_new in place of that key's pool rows (so no workgroup
+// reads a row another one writes) and stores both into the pool.  The
+// rotation is the one the rotary write performs, bit for bit.
 // ---------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, bool FUSED>
 __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
     const uint16_t *__restrict__ q, uint16_t *__restrict__ out, float *__restrict__ o_part,
-    float *__restrict__ lse_part, const uint16_t *__restrict__ k_layer,
-    const uint16_t *__restrict__ v_layer, int64_t pool_slots, int n_kv,
+    float *__restrict__ lse_part, uint16_t *__restrict__ k_layer,
+    uint16_t *__restrict__ v_layer, int64_t pool_slots, int n_kv,
     const int32_t *__restrict__ req_to_token, int num_reqs, int max_ctx_len,
     const int32_t *__restrict__ req_pool_indices, const int32_t *__restrict__ kv_indptr,
-    int n_heads, int chunk, int n_splits, float scale_log2) {
+    int n_heads, int chunk, int n_splits, float scale_log2, const uint16_t *__restrict__ k_new,
+    const uint16_t *__restrict__ v_new, const float2 *__restrict__ tab, int max_pos) {
     constexpr int KS = D / 32;          // k-steps of S^T
     constexpr int DB = D / 16;          // 16-row blocks of O^T
     constexpr int CK = 32;              // keys per wave chunk
@@ -264,6 +273,18 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
                                q + (static_cast<int64_t>(b) * n_heads + kvh * G + j) * D + 32 * ks + 8 * g)
                          : make_uint4(0, 0, 0, 0);
     }
+    const int npos = L - 1;                      // position of the step's new token
+    const bool fuse = FUSED && npos >= 0 && npos < max_pos;
+    if (fuse) {
+        // rotate q: lane (g, j) holds d = 32ks + 8g .. +7 of head j, pairs 16ks + 4g ..
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            Vec<bf16_t> x;
+            x.raw = qf[ks].u;
+            rotate_slice(x, tab + static_cast<int64_t>(npos) * (D / 2) + 16 * ks + 4 * g);
+            qf[ks].u = j < G ? x.raw : make_uint4(0, 0, 0, 0);
+        }
+    }
     f32x4_t o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -296,6 +317,31 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
             } else {
                 kx[i] = make_uint4(0, 0, 0, 0);
                 vx[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        if (fuse && c0 <= npos && npos < c0 + CK) {
+            // the chunk holding the new token: the lanes of its row (load im)
+            // take the rotated k_new and v_new instead of the pool, and store
+            // them there
+            const int kn = npos - c0 - rr;
+            if (kn >= 0 && kn % RPI == 0) {
+                const int im = kn / RPI;
+                const int64_t src = (static_cast<int64_t>(b) * n_kv + kvh) * D + 8 * cc;
+                Vec<bf16_t> x;
+                x.raw = *reinterpret_cast<const uint4 *>(k_new + src);
+                rotate_slice(x, tab + static_cast<int64_t>(npos) * (D / 2) + 4 * cc);
+                const uint4 nv = *reinterpret_cast<const uint4 *>(v_new + src);
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    kx[i] = i == im ? x.raw : kx[i];
+                    vx[i] = i == im ? nv : vx[i];
+                }
+                const int64_t nslot = row[npos];
+                if (nslot >= 0 && nslot < pool_slots) {
+                    const int64_t off = (nslot * n_kv + kvh) * D + 8 * cc;
+                    *reinterpret_cast<uint4 *>(k_layer + off) = x.raw;
+                    *reinterpret_cast<uint4 *>(v_layer + off) = nv;
+                }
             }
         }
         // bit k: key c0 + k exists and has a valid slot
@@ -472,12 +518,15 @@ hipError_t launch_decode_typed(const DecodeArgs &a, hipStream_t s) {
     const int n_kv = a.pool.n_kv_heads;
     const int64_t blocks = static_cast<int64_t>(a.batch) * a.n_splits * n_kv;
     if constexpr (sizeof(T) == 2) {
-        hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+        auto kern = a.k_new ? decode_mfma_kernel<D, G, true> : decode_mfma_kernel<D, G, false>;
+        hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                            static_cast<const uint16_t *>(a.q), static_cast<uint16_t *>(a.out), a.o_part,
-                           a.lse_part, static_cast<const uint16_t *>(a.pool.k_layer),
-                           static_cast<const uint16_t *>(a.pool.v_layer), a.pool.pool_slots, n_kv,
+                           a.lse_part, static_cast<uint16_t *>(a.pool.k_layer),
+                           static_cast<uint16_t *>(a.pool.v_layer), a.pool.pool_slots, n_kv,
                            a.req_to_token, a.num_reqs, a.max_ctx_len, a.req_pool_indices, a.kv_indptr,
-                           a.n_heads, a.split_chunk, a.n_splits, a.scale_log2);
+                           a.n_heads, a.split_chunk, a.n_splits, a.scale_log2,
+                           static_cast<const uint16_t *>(a.k_new), static_cast<const uint16_t *>(a.v_new),
+                           reinterpret_cast<const float2 *>(a.freqs), a.max_pos);
     } else {
         hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                            s, static_cast<const T *>(a.q), static_cast<T *>(a.out), a.o_part, a.lse_part,

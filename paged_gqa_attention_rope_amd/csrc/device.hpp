@@ -88,6 +88,26 @@ __device__ __forceinline__ float exp2_sub(float x, float m) {
     return x == -INFINITY ? 0.f : exp2f(x - m);
 }
 
+// Rotate one 16-byte slice (E/2 adjacent pairs) by the table entries cs[0..E/2):
+// (a, b) -> (a cos - b sin, a sin + b cos), evaluated in float64 (products of
+// float32-or-narrower values are exact there), then rounded to float32 and
+// stored as T.  The rotary write and the fused decode share it, so both store
+// identical bits.
+template <typename T>
+__device__ __forceinline__ void rotate_slice(Vec<T> &x, const float2 *cs) {
+    constexpr int E = Vec<T>::N;
+    float f[E];
+    x.to_float(f);
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+        const float2 c = cs[j];
+        const double a = f[2 * j], b = f[2 * j + 1];
+        f[2 * j] = static_cast<float>(a * c.x - b * static_cast<double>(c.y));
+        f[2 * j + 1] = static_cast<float>(a * c.y + b * static_cast<double>(c.x));
+    }
+    x.from_float(f);
+}
+
 // KV length of batch entry b, clamped to [0, cap]; 0 when its request row is
 // outside the table.  Keeps every req_to_token read inside the table even
 // when the device metadata is inconsistent.

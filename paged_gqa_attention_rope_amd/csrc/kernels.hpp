@@ -45,6 +45,11 @@ struct DecodeArgs {
     int split_chunk;
     int n_splits;
     float scale_log2;       // sm_scale * log2(e)
+    // fused rotary write of the step's new token (null k_new: plain decode)
+    const void *k_new;
+    const void *v_new;
+    const float *freqs;
+    int max_pos;
 };
 
 struct PrefillArgs {

@@ -69,25 +69,13 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(
         src = k + (static_cast<int64_t>(t) * n_kv + h) * D + vi * E;
         dst = k_layer + (slot * n_kv + h) * D + vi * E;
     }
+    // float64 arithmetic: a*cos and b*sin of float32-or-narrower operands are
+    // exact, so the stored value is the correctly rounded rotation by the
+    // table even when a*cos and b*sin nearly cancel
     Vec<T> x;
     x.load(src);
-    float f[E];
-    x.to_float(f);
-    const float2 *cs = tab + static_cast<int64_t>(pos) * (D / 2) + vi * (E / 2);
-#pragma unroll
-    for (int j = 0; j < E / 2; ++j) {
-        // float64: a*cos and b*sin of float32-or-narrower operands are exact, so
-        // the only roundings are one float64 rounding and the final store, and
-        // the stored value is the correctly rounded rotation by the table even
-        // when a*cos and b*sin nearly cancel.
-        const float2 c = cs[j];
-        const double a = f[2 * j], b = f[2 * j + 1];
-        f[2 * j] = static_cast<float>(a * c.x - b * static_cast<double>(c.y));
-        f[2 * j + 1] = static_cast<float>(a * c.y + b * static_cast<double>(c.x));
-    }
-    Vec<T> y;
-    y.from_float(f);
-    y.store(dst);
+    rotate_slice(x, tab + static_cast<int64_t>(pos) * (D / 2) + vi * (E / 2));
+    x.store(dst);
 }
 
 // Gradient of the rotation, in place: each pair is multiplied by the complex

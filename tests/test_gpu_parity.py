@@ -216,6 +216,33 @@ def test_decode_parity(name):
         E.assert_close(got[b], want[b], cs.dtype, f"{name} request {b} (L={cs.seq_lens[b]})")
 
 
+FUSED = [n for n in DECODE if n not in ("cfg1", "g2-d128-f32", "g4-d64-f32-page1")]   # bf16, one new token each
+
+
+@pytest.mark.parametrize("name", FUSED)
+def test_decode_attn_write_equals_write_then_decode(name):
+    # the fused call must store the same pool bits and produce the same output
+    # bits as the rotary write followed by the plain decode, on two separately
+    # staged copies of the workload (NaN canary everywhere else in the pools)
+    cs = DECODE[name]()
+    say(f"fused decode write case={name} seed={cs.seed} B={cs.batch} C={cs.split_chunk}")
+    assert cs.dtype == "bf16" and np.all(cs.new_lens == 1)
+    two = staging.stage(cs)
+    staging.run_write(two)
+    want_out = staging.run_decode(two)
+    one = staging.stage(cs)
+    got_out = astr.decode_attn_write(one.q, one.k, one.v, one.attn_cache, cs.layer_id, one.freqs,
+                                     cs.split_chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(got_out.view(torch.int16), want_out.view(torch.int16)), "output bits differ"
+    for a, b in ((one.k_buffer, two.k_buffer), (one.v_buffer, two.v_buffer)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "pool bits differ"
+    want = E.expected_decode(cs)
+    got = to_np(got_out)
+    for b in range(cs.batch):
+        E.assert_close(got[b], want[b], cs.dtype, f"{name} request {b}")
+
+
 def test_decode_split_partials_match_oracle():
     cs = _dec(41, batch=4, len_lo=100, len_hi=900, split_chunk=128)
     say("decode split partials chunk=128")

@@ -213,6 +213,18 @@ def test_attention_calls_validate_before_launch():
         assert st == want, (change, st)
     st = so.astr_decode_attn(None, None, 8, ctypes.byref(m), 5, 64, 0.0, None, None, None)
     assert st == L.ASTR_E_INVAL                          # layer out of range
+    # the fused decode write: table first, then its own checks
+    mt = L.KvMeta.from_buffer_copy(m)
+    mt.req_to_token = mt.req_pool_indices = mt.kv_indptr = 0x4000
+    mt.num_reqs, mt.max_ctx_len = 1, 8
+    q = ctypes.c_void_p(0x2000)
+    assert so.astr_decode_attn_write(q, q, q, q, 8, ctypes.byref(mt), 0, q, 4, 64, 0.0, None, None,
+                                     None) == L.ASTR_E_INVAL              # max_pos 4 < max_len 8
+    assert so.astr_decode_attn_write(q, None, q, q, 8, ctypes.byref(mt), 0, q, 8, 64, 0.0, None, None,
+                                     None) == L.ASTR_E_INVAL              # k_new missing
+    mt.kv_dtype = L.ASTR_F32
+    assert so.astr_decode_attn_write(q, q, q, q, 8, ctypes.byref(mt), 0, q, 8, 64, 0.0, None, None,
+                                     None) == L.ASTR_E_UNSUPPORTED        # bf16 only
     st = so.astr_rope_kv_write(None, None, None, None, None, 0, 8, None, 1, ctypes.byref(m), 0, None)
     assert st == L.ASTR_OK                               # zero tokens: a no-op
     st = so.astr_rope_table(None, 10, 64, 10000.0, None)
