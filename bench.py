@@ -164,6 +164,17 @@ def measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream
     fused_ms = _time_ms(lambda: astr.decode_attn_write(
         q_unrot, st_d.k, st_d.v, st_d.attn_cache, cs_d.layer_id, st_d.freqs, cs_d.split_chunk,
         out=out_d, o_part=o_part, lse_part=lse_part), stream)
+    # the whole step over all layers: one metadata build, every layer's fused
+    # decode write, eager and as one replayed HIP graph
+    from paged_gqa_attention_rope_amd.step import DecodeStep
+    nl = int(st_d.k_buffer.shape[0])
+    lay = DecodeStep(st_d.attn_cache, st_d.freqs, q_unrot.expand(nl, *q_unrot.shape).contiguous(),
+                     st_d.k.expand(nl, *st_d.k.shape).contiguous(),
+                     st_d.v.expand(nl, *st_d.v.shape).contiguous(), cs_d.split_chunk)
+    eager_ms = _time_ms(lay.run, stream, reps=3, warm=1)
+    lay.capture()
+    graph_ms = _time_ms(lay.replay, stream, reps=3, warm=1)
+    del lay
     g = st_p.q.clone()
     t, h, d = (int(x) for x in g.shape)
     rb_bytes = 2 * g.numel() * g.element_size() + t * (d // 2) * 8    # grad read + written, table rows
@@ -174,6 +185,10 @@ def measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream
             "write_then_decode_ms": round(write_then_decode_ms, 5),
             "achieved_GBps": round(dbytes / (fused_ms * 1e-3) / 1e9, 2),
             "frac": round(dbytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "decode_step_all_layers": {
+            "layers": nl, "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
+            "graph_ms_per_layer": round(graph_ms / nl, 5),
+            "achieved_GBps": round(nl * dbytes / (graph_ms * 1e-3) / 1e9, 2)},
         "rope_backward": {
             "shape": [t, h, d], "dtype": "bf16", "bytes_per_launch": rb_bytes,
             "ms_per_launch": round(rb_ms, 5),

@@ -225,20 +225,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 // FUSED: the step's new token is rotated and written here (inference.md,
 // "Attention Backend": the decode op takes the new k/v and writes them to the
 // cache).  q arrives unrotated and every workgroup rotates its G heads at
-// position L_b - 1; the workgroup whose split holds key L_b - 1 rotates
-// k_new, uses it and v_new in place of that key's pool rows (so no workgroup
-// reads a row another one writes) and stores both into the pool.  The
-// rotation is the one the rotary write performs, bit for bit.
+// position L_b - 1; the wave whose chunks hold key L_b - 1 rotates k_new,
+// uses it and v_new in place of that key's pool rows in its LDS tile and
+// stores both into the pool (k_store / v_store alias the pool; only that wave
+// loads the new token's rows, and it discards what it loaded there).
+// The rotation is the one the rotary write performs, bit for bit.
 // ---------------------------------------------------------------------------
 template <int D, int G, bool FUSED>
 __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
     const uint16_t *__restrict__ q, uint16_t *__restrict__ out, float *__restrict__ o_part,
-    float *__restrict__ lse_part, uint16_t *__restrict__ k_layer,
-    uint16_t *__restrict__ v_layer, int64_t pool_slots, int n_kv,
+    float *__restrict__ lse_part, const uint16_t *__restrict__ k_layer,
+    const uint16_t *__restrict__ v_layer, int64_t pool_slots, int n_kv,
     const int32_t *__restrict__ req_to_token, int num_reqs, int max_ctx_len,
     const int32_t *__restrict__ req_pool_indices, const int32_t *__restrict__ kv_indptr,
     int n_heads, int chunk, int n_splits, float scale_log2, const uint16_t *__restrict__ k_new,
-    const uint16_t *__restrict__ v_new, const float2 *__restrict__ tab, int max_pos) {
+    const uint16_t *__restrict__ v_new, const float2 *__restrict__ tab, int max_pos, uint16_t *k_store,
+    uint16_t *v_store) {
     constexpr int KS = D / 32;          // k-steps of S^T
     constexpr int DB = D / 16;          // 16-row blocks of O^T
     constexpr int CK = 32;              // keys per wave chunk
@@ -263,8 +265,11 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
     // cross-wave merge
     constexpr int T_BYTES = WAVES * CK * LDV * 2;
     constexpr int M_BYTES = WAVES * G * (D + 2) * 4;
-    __shared__ __attribute__((aligned(16))) char smem[T_BYTES > M_BYTES ? T_BYTES : M_BYTES];
+    constexpr int S_BYTES = T_BYTES > M_BYTES ? T_BYTES : M_BYTES;
+    constexpr int N_BYTES = FUSED ? 4 * D : 0;     // the new token's rotated k and v rows
+    __shared__ __attribute__((aligned(16))) char smem[S_BYTES + N_BYTES];
     uint16_t *sT = reinterpret_cast<uint16_t *>(smem) + wave * CK * LDV;
+    uint16_t *s_new = reinterpret_cast<uint16_t *>(smem + S_BYTES);
 
     Frag8 qf[KS];
 #pragma unroll
@@ -303,6 +308,27 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
         const int key = c + (lane & 31);
         return key < end ? row[key] : -1;
     };
+    // the new token: lanes 0 .. D/8 - 1 of the wave whose chunks hold key
+    // L - 1 rotate slice `lane` of k_new, store it and v_new into the pool and
+    // stage both in LDS for that chunk's tile (only this wave loads the new
+    // token's rows from the pool, and it replaces what it loaded there)
+    const bool has_new = fuse && npos >= start && npos < end && ((npos - start) / CK) % WAVES == wave &&
+                         rr == 0;
+    if (has_new) {
+        const int64_t src = (static_cast<int64_t>(b) * n_kv + kvh) * D + 8 * cc;
+        Vec<bf16_t> x;
+        x.raw = *reinterpret_cast<const uint4 *>(k_new + src);
+        rotate_slice(x, tab + static_cast<int64_t>(npos) * (D / 2) + 4 * cc);
+        const uint4 nv = *reinterpret_cast<const uint4 *>(v_new + src);
+        *reinterpret_cast<uint4 *>(s_new + 8 * cc) = x.raw;
+        *reinterpret_cast<uint4 *>(s_new + D + 8 * cc) = nv;
+        const int64_t nslot = row[npos];
+        if (nslot >= 0 && nslot < pool_slots) {
+            const int64_t off = (nslot * n_kv + kvh) * D + 8 * cc;
+            *reinterpret_cast<uint4 *>(k_store + off) = x.raw;
+            *reinterpret_cast<uint4 *>(v_store + off) = nv;
+        }
+    }
     int32_t sl_now = slot_of(start + wave * CK);
     for (int c0 = start + wave * CK; c0 < end; c0 += WAVES * CK) {
         const int32_t sl_next = slot_of(c0 + WAVES * CK);
@@ -319,37 +345,16 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
                 vx[i] = make_uint4(0, 0, 0, 0);
             }
         }
-        if (fuse && c0 <= npos && npos < c0 + CK) {
-            // the chunk holding the new token: the lanes of its row (load im)
-            // take the rotated k_new and v_new instead of the pool, and store
-            // them there
-            const int kn = npos - c0 - rr;
-            if (kn >= 0 && kn % RPI == 0) {
-                const int im = kn / RPI;
-                const int64_t src = (static_cast<int64_t>(b) * n_kv + kvh) * D + 8 * cc;
-                Vec<bf16_t> x;
-                x.raw = *reinterpret_cast<const uint4 *>(k_new + src);
-                rotate_slice(x, tab + static_cast<int64_t>(npos) * (D / 2) + 4 * cc);
-                const uint4 nv = *reinterpret_cast<const uint4 *>(v_new + src);
-#pragma unroll
-                for (int i = 0; i < NI; ++i) {
-                    kx[i] = i == im ? x.raw : kx[i];
-                    vx[i] = i == im ? nv : vx[i];
-                }
-                const int64_t nslot = row[npos];
-                if (nslot >= 0 && nslot < pool_slots) {
-                    const int64_t off = (nslot * n_kv + kvh) * D + 8 * cc;
-                    *reinterpret_cast<uint4 *>(k_layer + off) = x.raw;
-                    *reinterpret_cast<uint4 *>(v_layer + off) = nv;
-                }
-            }
-        }
+        // the chunk holding the new token: its row of the LDS tile takes the
+        // rotated k_new / v_new staged above
+        const bool mine = has_new && c0 <= npos && npos < c0 + CK;
         // bit k: key c0 + k exists and has a valid slot
         const uint32_t okmask = static_cast<uint32_t>(
             __ballot(c0 + (lane & 31) < end && sl_now >= 0 && sl_now < pool_slots) & 0xffffffffull);
         // K rows -> LDS -> MFMA A-operand layout (lane: key 16kb + j, d = 32ks + 8g)
 #pragma unroll
         for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4 *>(sT + (i * RPI + rr) * LDV + 8 * cc) = kx[i];
+        if (mine) *reinterpret_cast<uint4 *>(sT + (npos - c0) * LDV + 8 * cc) = *reinterpret_cast<const uint4 *>(s_new + 8 * cc);
         wave_lds_fence();
         Frag8 kf[2][KS];
 #pragma unroll
@@ -361,6 +366,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
         wave_lds_fence();                       // K read out before V overwrites the tile
 #pragma unroll
         for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4 *>(sT + (i * RPI + rr) * LDV + 8 * cc) = vx[i];
+        if (mine) *reinterpret_cast<uint4 *>(sT + (npos - c0) * LDV + 8 * cc) = *reinterpret_cast<const uint4 *>(s_new + D + 8 * cc);
         f32x4_t sc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -521,12 +527,13 @@ hipError_t launch_decode_typed(const DecodeArgs &a, hipStream_t s) {
         auto kern = a.k_new ? decode_mfma_kernel<D, G, true> : decode_mfma_kernel<D, G, false>;
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                            static_cast<const uint16_t *>(a.q), static_cast<uint16_t *>(a.out), a.o_part,
-                           a.lse_part, static_cast<uint16_t *>(a.pool.k_layer),
-                           static_cast<uint16_t *>(a.pool.v_layer), a.pool.pool_slots, n_kv,
+                           a.lse_part, static_cast<const uint16_t *>(a.pool.k_layer),
+                           static_cast<const uint16_t *>(a.pool.v_layer), a.pool.pool_slots, n_kv,
                            a.req_to_token, a.num_reqs, a.max_ctx_len, a.req_pool_indices, a.kv_indptr,
                            a.n_heads, a.split_chunk, a.n_splits, a.scale_log2,
                            static_cast<const uint16_t *>(a.k_new), static_cast<const uint16_t *>(a.v_new),
-                           reinterpret_cast<const float2 *>(a.freqs), a.max_pos);
+                           reinterpret_cast<const float2 *>(a.freqs), a.max_pos,
+                           static_cast<uint16_t *>(a.pool.k_layer), static_cast<uint16_t *>(a.pool.v_layer));
     } else {
         hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                            s, static_cast<const T *>(a.q), static_cast<T *>(a.out), a.o_part, a.lse_part,

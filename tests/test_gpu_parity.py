@@ -243,6 +243,39 @@ def test_decode_attn_write_equals_write_then_decode(name):
         E.assert_close(got[b], want[b], cs.dtype, f"{name} request {b}")
 
 
+def test_decode_step_graph_replays_equal_eager():
+    # a 4-layer step (history in one layer, zeros elsewhere) run eagerly on one
+    # staging and captured + replayed three times on another, with unrelated
+    # eager work between replays: outputs and pools must match bit for bit;
+    # the layer holding the history also matches the oracle
+    from paged_gqa_attention_rope_amd.step import DecodeStep
+    cs = _dec(51, batch=6, len_hi=1200, n_layers=4, random_layer=True, split_chunk=256)
+    say(f"graph-captured 4-layer decode step, history in layer {cs.layer_id}")
+    nl, b, hq, hk, d = cs.n_layers, cs.batch, cs.n_heads, cs.n_kv_heads, cs.head_dim
+    rng = np.random.default_rng(52)
+    inp = [bf16_storage(rng.standard_normal((nl, b, n, d)).astype(np.float32)) for n in (hq, hk, hk)]
+    inp[0][cs.layer_id], inp[1][cs.layer_id], inp[2][cs.layer_id] = cs.q, cs.k, cs.v
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in inp)
+    eager = staging.stage(cs, canary=False)
+    want = DecodeStep(eager.attn_cache, eager.freqs, q, k, v, cs.split_chunk).run().clone()
+    graphed = staging.stage(cs, canary=False)
+    step = DecodeStep(graphed.attn_cache, graphed.freqs, q, k, v, cs.split_chunk)
+    step.capture()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for r in range(3):
+        step.out.fill_(float("nan"))
+        got = step.replay()
+        scratch.add_(1.0)                           # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"replay {r} output differs"
+        for a_, b_ in ((graphed.k_buffer, eager.k_buffer), (graphed.v_buffer, eager.v_buffer)):
+            assert torch.equal(a_.view(torch.int16), b_.view(torch.int16)), f"replay {r} pool differs"
+    ref = E.expected_decode(cs)
+    got = to_np(want[cs.layer_id])
+    for i in range(b):
+        E.assert_close(got[i], ref[i], cs.dtype, f"layer {cs.layer_id} request {i}")
+
+
 def test_decode_split_partials_match_oracle():
     cs = _dec(41, batch=4, len_lo=100, len_hi=900, split_chunk=128)
     say("decode split partials chunk=128")
