@@ -29,6 +29,19 @@ q_tile rows each, the last one of a request possibly partial, and are listed
 heaviest first (by the KV extent their last row sees; ties by request, then
 tile index -- the pages fix only the tile -> request maps, not their order);
 ``out_cache_loc`` is flat in ``qo_indptr`` order.
+
+Lifecycle (same pages: the allocator's reference counts and LRU eviction;
+the completion rule that records the prompt plus the generated tokens already
+decoded into KV, never the final sampled token, and releases the partial
+page).  Readings where the pages are silent: a cached page is evictable when
+only the radix still holds it and it has no cached children (evicting a
+parent first would orphan its children); the least recently used one goes
+first, where a lookup that matches a page and an insert that passes over it
+both use it, each call counting as one tick; an ``extend`` short of free pages
+first evicts just enough of them, and when even evicting every evictable page
+would not be enough it evicts nothing and fails; a page is cached at most once
+(an insert that would cache an already cached page under another prefix
+stops there).
 """
 
 import numpy as np
@@ -44,12 +57,16 @@ class PoolError(Exception):
 
 
 class _Node:
-    __slots__ = ("page", "parent", "digest")
+    __slots__ = ("page", "parent", "digest", "key", "n_children", "stamp", "serial")
 
-    def __init__(self, page, parent, digest):
+    def __init__(self, page, parent, digest, key=None, serial=0):
         self.page = page
         self.parent = parent
         self.digest = digest      # for introspection only
+        self.key = key            # its entry in PagePool.children
+        self.n_children = 0
+        self.stamp = 0            # tick of its last use
+        self.serial = serial      # creation order
 
 
 class PagePool:
@@ -80,6 +97,10 @@ class PagePool:
         self.ref = [0] * self.n_pages
         self.children = {}                                # (parent id, token tuple) -> node
         self.root = _Node(None, None, None)
+        self.node_of_page = {}                            # cached page -> its node
+        self.clock = 0
+        self.n_created = 0
+        self.evicted = 0                                  # pages evicted so far
 
     # -- helpers --------------------------------------------------------------
     def _slot(self, req: int, pos: int) -> int:
@@ -111,11 +132,13 @@ class PagePool:
             raise PoolError("nomem", "no free request slot")
         matched = []
         if self._radix_on() and tokens is not None and n_tokens > 0:
+            self.clock += 1
             node = self.root
             for k in range((n_tokens - 1) // self.page_size):
                 child = self.children.get((id(node), self._page_tokens(tokens, k)))
                 if child is None:
                     break
+                child.stamp = self.clock
                 matched.append(child.page)
                 node = child
         self.live[req] = True
@@ -138,7 +161,9 @@ class PagePool:
         if self.mode == 1:
             need = -(-new // self.page_size) - len(self.pages[req])
             if need > self.n_free:
-                raise PoolError("nomem", "pool exhausted")
+                if need > self.n_free + self.evictable_pages():
+                    raise PoolError("nomem", "pool exhausted")
+                self.evict(need - self.n_free)
             for _ in range(max(need, 0)):
                 lp = self.free.index(True, self.first_free)
                 self.first_free = lp + 1
@@ -188,15 +213,22 @@ class PagePool:
         if not self._radix_on():
             return
         n_full = min(int(n_materialized), self.length[req]) // self.page_size
+        self.clock += 1
         node = self.root
         for k in range(n_full):
             key = (id(node), self._page_tokens(tokens, k))
             child = self.children.get(key)
             if child is None:
                 page = self.pages[req][k]
-                child = _Node(page, node, hash(key[1]))
+                if page in self.node_of_page:
+                    break                 # already cached under another prefix
+                child = _Node(page, node, hash(key[1]), key, self.n_created)
+                self.n_created += 1
                 self.children[key] = child
+                self.node_of_page[page] = child
+                node.n_children += 1
                 self.ref[page] += 1
+            child.stamp = self.clock
             node = child
 
     def release(self, req: int):
@@ -213,3 +245,52 @@ class PagePool:
         self.length[req] = 0
         self.live[req] = False
         self.table[req, :] = -1
+
+    def complete(self, req: int, tokens, n_tokens: int):
+        """A finished request: ``tokens[:n_tokens]`` is its prompt plus every
+        generated token, the last one sampled but never run through the model,
+        so only the first n_tokens - 1 have KV; cache their complete pages, then
+        release the request (its partial page with it)."""
+        self._check_live(req)
+        if n_tokens > 1:
+            self.insert(req, tokens, n_tokens - 1)
+        self.release(req)
+
+    # -- eviction ----------------------------------------------------------------
+    def _evictable_leaves(self):
+        return [n for n in self.node_of_page.values()
+                if n.n_children == 0 and self.ref[n.page] == 1]
+
+    def evictable_pages(self) -> int:
+        """Cached pages that repeated leaf eviction could free: those with no
+        page in their cached subtree (themselves included) held by a request."""
+        pinned = set()
+        for n in self.node_of_page.values():
+            if self.ref[n.page] > 1:
+                while n is not self.root and id(n) not in pinned:
+                    pinned.add(id(n))
+                    n = n.parent
+        return len(self.node_of_page) - len(pinned)
+
+    def evict(self, n_pages: int) -> int:
+        """Free up to n_pages cached pages, least recently used leaf first
+        (ties: the earlier created); returns how many were freed."""
+        done = 0
+        while done < n_pages:
+            leaves = self._evictable_leaves()
+            if not leaves:
+                break
+            n = min(leaves, key=lambda x: (x.stamp, x.serial))
+            del self.children[n.key]
+            del self.node_of_page[n.page]
+            n.parent.n_children -= 1
+            self.ref[n.page] -= 1
+            self.free[n.page] = True
+            self.n_free += 1
+            self.first_free = min(self.first_free, n.page)
+            done += 1
+        self.evicted += done
+        return done
+
+    def cached_pages(self) -> int:
+        return len(self.node_of_page)
