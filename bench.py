@@ -180,6 +180,7 @@ def measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream
     rb_bytes = 2 * g.numel() * g.element_size() + t * (d // 2) * 8    # grad read + written, table rows
     rb_ms = _time_ms(lambda: astr.rope_backward(g, st_p.positions, st_p.freqs), stream)
     return {
+        "pagepool_lifecycle": measure_pagepool_lifecycle(),
         "decode_attn_write": {
             "workload": cs_d.name, "ms_per_launch": round(fused_ms, 5),
             "write_then_decode_ms": round(write_then_decode_ms, 5),
@@ -195,6 +196,56 @@ def measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream
             "achieved_GBps": round(rb_bytes / (rb_ms * 1e-3) / 1e9, 2),
             "frac": round(rb_bytes / (rb_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+
+
+def measure_pagepool_lifecycle(n_requests=1536, batch=16, decode_steps=8, seed=6):
+    """Host cost of the page-table builder's whole request lifecycle, through
+    the Python binding, on a pool shaped like the prefill workload (page 16,
+    65 536 slots) and too small to keep every finished prompt: batches of 16
+    requests, each a prompt of one of 4 shared prefixes (16 * U{0..128}
+    tokens) plus its own U{32..512} tokens, are admitted (radix lookup),
+    extended, bound as one prefill step, run 8 decode steps (extend by one and
+    bind each), then completed (cache the pages with KV, release)."""
+    import paged_gqa_attention_rope_amd as astr
+    rng = np.random.default_rng(seed)
+    ps, slots, max_ctx = 16, 65536, 2560
+    pp = astr.PagePool(1, slots, ps, batch, max_ctx)
+    prefixes = [rng.integers(0, 32000, size=2048).astype(np.int32) for _ in range(4)]
+    admitted = cached = 0
+    t0 = time.perf_counter()
+    t_bind = 0.0
+    n_bind = 0
+    for first in range(0, n_requests, batch):
+        reqs, toks, lens, new = [], [], [], []
+        for _ in range(min(batch, n_requests - first)):
+            pre = prefixes[rng.integers(0, 4)][:ps * int(rng.integers(0, 129))]
+            own = rng.integers(0, 32000, size=int(rng.integers(32, 513))).astype(np.int32)
+            t = np.concatenate([pre, own, rng.integers(0, 32000, size=decode_steps).astype(np.int32)])
+            n = len(pre) + len(own)
+            r, c = pp.admit(t, n)
+            pp.extend(r, n - c)
+            reqs.append(r); toks.append(t); lens.append(n); new.append(n - c)
+            admitted += n
+            cached += c
+        tb = time.perf_counter()
+        pp.bind(reqs, new, 64)
+        t_bind += time.perf_counter() - tb
+        n_bind += 1
+        for _ in range(decode_steps):
+            for r in reqs:
+                pp.extend(r, 1)
+            tb = time.perf_counter()
+            pp.bind(reqs, [1] * len(reqs), 64)
+            t_bind += time.perf_counter() - tb
+            n_bind += 1
+        for r, t, n in zip(reqs, toks, lens):
+            pp.complete(r, t, n + decode_steps)
+    total = time.perf_counter() - t0
+    return {"requests": n_requests, "batch": batch, "decode_steps": decode_steps,
+            "pool_pages": slots // ps, "us_per_request": round(total / n_requests * 1e6, 2),
+            "us_per_bind": round(t_bind / n_bind * 1e6, 2),
+            "prefix_hit_frac": round(cached / admitted, 4), "pages_evicted": pp.evicted_pages(),
+            "pages_cached_at_end": pp.cached_pages()}
 
 
 def main():

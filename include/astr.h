@@ -275,9 +275,10 @@ void astr_pagepool_destroy(astr_pagepool *pp);
 int astr_pagepool_admit(astr_pagepool *pp, const int32_t *tokens, int n_tokens,
                         int *req_idx, int *cached_len);
 
-/* Give request req_idx slots for positions [len, len + n_new).
- * Errors: INVAL (not live, or length > max_ctx_len), NOMEM (pool exhausted;
- * nothing changes). */
+/* Give request req_idx slots for positions [len, len + n_new), evicting
+ * least recently used cached pages first when the free pages are short (see
+ * astr_pagepool_evict).  Errors: INVAL (not live, or length > max_ctx_len),
+ * NOMEM (free plus evictable pages are short; nothing changes). */
 int astr_pagepool_extend(astr_pagepool *pp, int req_idx, int n_new);
 
 /* Per-step metadata for batch entries b < batch (request req_idx[b], q_lens[b]
@@ -304,6 +305,30 @@ int astr_pagepool_insert(astr_pagepool *pp, int req_idx, const int32_t *tokens,
 /* Drop the request's page references (pages reaching zero are freed) and
  * free its request slot; its table row returns to -1. */
 int astr_pagepool_release(astr_pagepool *pp, int req_idx);
+
+/* A finished request (inference.md, "KVCache System": what completion
+ * records).  tokens host [n_tokens] is its prompt plus every generated token;
+ * the last one was sampled but never passed through the model, so only the
+ * first n_tokens - 1 have KV: the complete pages among those are cached as by
+ * astr_pagepool_insert, then the request is released (its partial page and
+ * every page no one else holds return to the free set).
+ * Errors: INVAL (not live, tokens NULL with n_tokens > 0). */
+int astr_pagepool_complete(astr_pagepool *pp, int req_idx, const int32_t *tokens, int n_tokens);
+
+/* LRU eviction (same section: the allocator's ref-counted pages with LRU
+ * eviction).  A cached page is evictable when only the radix holds it and it
+ * has no cached children; the least recently used goes first, where each
+ * admit or insert call is one tick and uses every cached page it matches or
+ * passes over.  astr_pagepool_extend evicts by itself when the free pages are
+ * short, just enough of them, and evicts nothing when even all evictable
+ * pages would not be enough (NOMEM).  This call frees up to n_pages cached
+ * pages ahead of need and returns how many it freed (0 without radix
+ * sharing; -1 and INVAL on a bad argument). */
+int64_t astr_pagepool_evict(astr_pagepool *pp, int64_t n_pages);
+
+/* Introspection: pages held by the radix; pages evicted since creation. */
+int64_t astr_pagepool_cached_pages(const astr_pagepool *pp);
+int64_t astr_pagepool_evicted_pages(const astr_pagepool *pp);
 
 /* The host table [max_reqs, max_ctx_len] int32 owned by the handle, valid
  * until the next call that changes it or destroy (NULL on bad handle). */

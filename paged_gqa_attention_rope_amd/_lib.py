@@ -21,7 +21,8 @@ EXPORTS = (
     "astr_decode_attn", "astr_prefill_attn", "astr_pagepool_create", "astr_pagepool_destroy",
     "astr_pagepool_admit", "astr_pagepool_extend", "astr_pagepool_bind", "astr_pagepool_insert",
     "astr_pagepool_release", "astr_pagepool_table", "astr_pagepool_free_pages",
-    "astr_pagepool_page_ref",
+    "astr_pagepool_page_ref", "astr_pagepool_complete", "astr_pagepool_evict",
+    "astr_pagepool_cached_pages", "astr_pagepool_evicted_pages",
 )
 
 c_int, c_i32p, c_vp = ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
@@ -81,6 +82,13 @@ def lib():
     L.astr_pagepool_free_pages.argtypes = [c_vp]
     L.astr_pagepool_free_pages.restype = ctypes.c_int64
     L.astr_pagepool_page_ref.argtypes = [c_vp, ctypes.c_int64]
+    L.astr_pagepool_complete.argtypes = [c_vp, c_int, c_i32p, c_int]
+    L.astr_pagepool_evict.argtypes = [c_vp, ctypes.c_int64]
+    L.astr_pagepool_evict.restype = ctypes.c_int64
+    L.astr_pagepool_cached_pages.argtypes = [c_vp]
+    L.astr_pagepool_cached_pages.restype = ctypes.c_int64
+    L.astr_pagepool_evicted_pages.argtypes = [c_vp]
+    L.astr_pagepool_evicted_pages.restype = ctypes.c_int64
     _lib = L
     return L
 

@@ -16,7 +16,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from ._lib import ASTR_BF16, ASTR_F32, KvMeta, check, lib
+from ._lib import ASTR_BF16, ASTR_E_INVAL, ASTR_F32, KvMeta, check, lib
 
 _DTYPES = {torch.float32: ASTR_F32, torch.bfloat16: ASTR_BF16}
 
@@ -347,6 +347,27 @@ class PagePool:
 
     def release(self, req: int):
         check(lib().astr_pagepool_release(self._h, int(req)))
+
+    def complete(self, req: int, tokens, n_tokens: Optional[int] = None):
+        """Finish a request: cache the complete pages of tokens[:n_tokens - 1]
+        (the final sampled token has no KV) and release it."""
+        tok = _i32(tokens)
+        n = int(tok.size if n_tokens is None else n_tokens)
+        _need(0 <= n <= tok.size, "n_tokens outside the tokens given")
+        check(lib().astr_pagepool_complete(self._h, int(req), _i32p(tok) if tok.size else None, n))
+
+    def evict(self, n_pages: int) -> int:
+        """Free up to n_pages cached pages, least recently used first."""
+        n = int(lib().astr_pagepool_evict(self._h, int(n_pages)))
+        if n < 0:
+            check(ASTR_E_INVAL)
+        return n
+
+    def cached_pages(self) -> int:
+        return int(lib().astr_pagepool_cached_pages(self._h))
+
+    def evicted_pages(self) -> int:
+        return int(lib().astr_pagepool_evicted_pages(self._h))
 
     def table(self) -> np.ndarray:
         """A copy of the host table [max_reqs, max_ctx_len] int32."""

@@ -8,10 +8,21 @@
 // optional permutation.  The radix keys a child by (parent node, 64-bit FNV-1a
 // digest of the page's tokens) only to find candidates; a match always
 // compares the stored token tuple exactly, so the digest never decides it.
+//
+// Lifecycle: a finished request caches the complete pages of its prompt and
+// of the generated tokens already decoded into KV (the final sampled token
+// has none), then releases everything else.  Under pool pressure the
+// allocator evicts cached pages that only the radix holds, least recently
+// used leaf first: a leaf, because evicting a parent would orphan its cached
+// children; recency is a tick per lookup or insert call, given to every node
+// the call passes over.  An extend evicts only when it must, and nothing at
+// all when evicting every evictable page would still leave it short.
 #include <cstdint>
 #include <algorithm>
 #include <cstring>
 #include <new>
+#include <set>
+#include <tuple>
 #include <unordered_map>
 #include <vector>
 
@@ -21,11 +32,17 @@
 namespace {
 
 struct Node {
-    int32_t page;                 // logical page id
-    int32_t parent;               // node index, -1 for children of the root
-    uint64_t digest;              // FNV-1a of the page's tokens (introspection, bucketing)
+    int32_t page = -1;            // logical page id (-1: the slot is unused)
+    int32_t parent = -1;          // node index, -1 for children of the root
+    int32_t n_children = 0;
+    uint64_t digest = 0;          // FNV-1a of the page's tokens (introspection, bucketing)
+    uint64_t stamp = 0;           // tick of its last use
+    uint64_t serial = 0;          // creation order
+    bool in_lru = false;          // listed in astr_pagepool::lru
     std::vector<int32_t> tokens;  // the exact page contents
 };
+
+using LruKey = std::tuple<uint64_t, uint64_t, int32_t>;   // (stamp, serial, node)
 
 struct KeyHash {
     size_t operator()(const std::pair<int32_t, uint64_t> &k) const {
@@ -64,9 +81,86 @@ struct astr_pagepool {
     int64_t free_hint = 0;                // no free page below word free_hint
     std::vector<int32_t> ref;
     std::vector<Node> nodes;
+    std::vector<int32_t> free_nodes;      // unused slots of nodes
     std::unordered_map<std::pair<int32_t, uint64_t>, std::vector<int32_t>, KeyHash> children;
+    std::vector<int32_t> node_of_page;    // cached page -> node (-1: not cached)
+    std::set<LruKey> lru;                 // evictable leaves, least recently used first
+    int64_t cached = 0;                   // pages held by the radix
+    int64_t evicted = 0;                  // pages evicted so far
+    uint64_t clock = 0;
+    uint64_t n_created = 0;
 
     bool radix_on() const { return mode == 1 && page_size > 1; }
+
+    // keep node n listed in lru exactly when it is an evictable leaf
+    void refresh(int32_t n) {
+        Node &nd = nodes[n];
+        if (nd.in_lru) {
+            lru.erase(LruKey{nd.stamp, nd.serial, n});
+            nd.in_lru = false;
+        }
+        if (nd.page >= 0 && nd.n_children == 0 && ref[nd.page] == 1) {
+            lru.insert(LruKey{nd.stamp, nd.serial, n});
+            nd.in_lru = true;
+        }
+    }
+
+    void touch(int32_t n) {
+        if (nodes[n].stamp == clock) return;
+        if (nodes[n].in_lru) lru.erase(LruKey{nodes[n].stamp, nodes[n].serial, n});
+        nodes[n].stamp = clock;
+        if (nodes[n].in_lru) lru.insert(LruKey{nodes[n].stamp, nodes[n].serial, n});
+    }
+
+    // a page's reference count changed: its node may enter or leave lru
+    void ref_changed(int32_t page) {
+        if (node_of_page.empty()) return;
+        int32_t n = node_of_page[page];
+        if (n >= 0) refresh(n);
+    }
+
+    // cached pages that repeated leaf eviction could free: those whose cached
+    // subtree (themselves included) holds no page a request still holds
+    int64_t evictable_pages() const {
+        std::vector<uint8_t> pinned(nodes.size(), 0);
+        int64_t n_pinned = 0;
+        for (size_t i = 0; i < nodes.size(); ++i) {
+            if (nodes[i].page < 0 || ref[nodes[i].page] <= 1) continue;
+            for (int32_t n = static_cast<int32_t>(i); n >= 0 && !pinned[n]; n = nodes[n].parent) {
+                pinned[n] = 1;
+                ++n_pinned;
+            }
+        }
+        return cached - n_pinned;
+    }
+
+    int64_t evict(int64_t want) {
+        int64_t done = 0;
+        while (done < want && !lru.empty()) {
+            const int32_t n = std::get<2>(*lru.begin());
+            lru.erase(lru.begin());
+            Node &nd = nodes[n];
+            nd.in_lru = false;
+            auto it = children.find({nd.parent, nd.digest});
+            auto &bucket = it->second;
+            bucket.erase(std::find(bucket.begin(), bucket.end(), n));
+            if (bucket.empty()) children.erase(it);
+            const int32_t page = nd.page, parent = nd.parent;
+            node_of_page[page] = -1;
+            nd.page = -1;
+            nd.tokens.clear();
+            free_nodes.push_back(n);
+            --cached;
+            if (--ref[page] == 0) give_back_page(page);
+            if (parent >= 0) {
+                --nodes[parent].n_children;
+                refresh(parent);
+            }
+            ++done;
+        }
+        evicted += done;
+        return done;
+    }
 
     int64_t slot_of(int req, int pos) const {
         if (mode == 0) return static_cast<int64_t>(req) * max_ctx_len + pos;
@@ -98,7 +192,9 @@ struct astr_pagepool {
         auto it = children.find({parent, fnv1a(tok, page_size)});
         if (it == children.end()) return -1;
         for (int32_t n : it->second) {
-            if (std::memcmp(nodes[n].tokens.data(), tok, sizeof(int32_t) * page_size) == 0) return n;
+            if (nodes[n].parent == parent &&
+                std::memcmp(nodes[n].tokens.data(), tok, sizeof(int32_t) * page_size) == 0)
+                return n;
         }
         return -1;
     }
@@ -142,6 +238,7 @@ extern "C" int astr_pagepool_create(astr_pagepool **out, int mode, int64_t pool_
             for (int64_t p = 0; p < pp->n_pages; ++p) pp->free_bits[p / 64] |= 1ull << (p % 64);
             pp->free_count = pp->n_pages;
             pp->ref.assign(pp->n_pages, 0);
+            if (pp->radix_on()) pp->node_of_page.assign(pp->n_pages, -1);
             if (page_perm) {
                 pp->perm.assign(page_perm, page_perm + pp->n_pages);
                 std::vector<uint8_t> seen(pp->n_pages, 0);
@@ -177,18 +274,23 @@ extern "C" int astr_pagepool_admit(astr_pagepool *pp, const int32_t *tokens, int
     if (req < 0) return astr::fail(ASTR_E_NOMEM, "pagepool_admit: no free request slot");
     std::vector<int32_t> matched;
     if (pp->radix_on() && tokens && n_tokens > 0) {
+        ++pp->clock;
         int32_t parent = -1;
         int max_pages = (n_tokens - 1) / pp->page_size;
         for (int k = 0; k < max_pages; ++k) {
             int n = pp->find_child(parent, tokens + static_cast<size_t>(k) * pp->page_size);
             if (n < 0) break;
+            pp->touch(n);
             matched.push_back(pp->nodes[n].page);
             parent = n;
         }
     }
     pp->live[req] = 1;
     pp->pages[req] = matched;
-    for (int32_t p : matched) ++pp->ref[p];
+    for (int32_t p : matched) {
+        ++pp->ref[p];
+        pp->ref_changed(p);
+    }
     int len = static_cast<int>(matched.size()) * pp->page_size;
     pp->length[req] = len;
     int32_t *row = pp->table.data() + static_cast<size_t>(req) * pp->max_ctx_len;
@@ -209,9 +311,14 @@ extern "C" int astr_pagepool_extend(astr_pagepool *pp, int req_idx, int n_new) {
     if (pp->mode == 1) {
         int64_t need = (static_cast<int64_t>(nw) + pp->page_size - 1) / pp->page_size -
                        static_cast<int64_t>(pp->pages[req_idx].size());
-        if (need > pp->free_count)
-            return astr::fail(ASTR_E_NOMEM, "pagepool_extend: need %lld pages, %lld free",
-                              static_cast<long long>(need), static_cast<long long>(pp->free_count));
+        if (need > pp->free_count) {
+            const int64_t can = pp->radix_on() ? pp->evictable_pages() : 0;
+            if (need > pp->free_count + can)
+                return astr::fail(ASTR_E_NOMEM, "pagepool_extend: need %lld pages, %lld free, %lld evictable",
+                                  static_cast<long long>(need), static_cast<long long>(pp->free_count),
+                                  static_cast<long long>(can));
+            pp->evict(need - pp->free_count);
+        }
         for (int64_t i = 0; i < need; ++i) {
             int64_t lp = pp->take_lowest_page();
             pp->ref[lp] = 1;
@@ -301,21 +408,44 @@ extern "C" int astr_pagepool_insert(astr_pagepool *pp, int req_idx, const int32_
         return astr::fail(ASTR_E_INVAL, "pagepool_insert: bad tokens");
     int n = n_materialized < pp->length[req_idx] ? n_materialized : pp->length[req_idx];
     int full = n / pp->page_size;
+    ++pp->clock;
     int32_t parent = -1;
     try {
         for (int k = 0; k < full; ++k) {
             const int32_t *tok = tokens + static_cast<size_t>(k) * pp->page_size;
             int c = pp->find_child(parent, tok);
             if (c < 0) {
-                Node nd;
-                nd.page = pp->pages[req_idx][k];
-                nd.parent = parent;
-                nd.digest = fnv1a(tok, pp->page_size);
+                const int32_t page = pp->pages[req_idx][k];
+                if (pp->node_of_page[page] >= 0) break;   // already cached under another prefix
+                if (pp->free_nodes.empty()) {
+                    pp->nodes.emplace_back();
+                    pp->free_nodes.push_back(static_cast<int32_t>(pp->nodes.size() - 1));
+                }
+                const uint64_t digest = fnv1a(tok, pp->page_size);
+                auto &bucket = pp->children[{parent, digest}];
+                bucket.reserve(bucket.size() + 1);
+                c = pp->free_nodes.back();
+                Node &nd = pp->nodes[c];
                 nd.tokens.assign(tok, tok + pp->page_size);
-                c = static_cast<int>(pp->nodes.size());
-                pp->nodes.push_back(std::move(nd));
-                pp->children[{parent, pp->nodes.back().digest}].push_back(c);
-                ++pp->ref[pp->nodes.back().page];
+                pp->free_nodes.pop_back();          // nothing below throws
+                bucket.push_back(c);
+                nd.page = page;
+                nd.parent = parent;
+                nd.n_children = 0;
+                nd.digest = digest;
+                nd.stamp = pp->clock;
+                nd.serial = pp->n_created++;
+                nd.in_lru = false;
+                pp->node_of_page[page] = c;
+                ++pp->cached;
+                ++pp->ref[page];
+                if (parent >= 0) {
+                    ++pp->nodes[parent].n_children;
+                    pp->refresh(parent);
+                }
+                pp->refresh(c);
+            } else {
+                pp->touch(c);
             }
             parent = c;
         }
@@ -331,6 +461,7 @@ extern "C" int astr_pagepool_release(astr_pagepool *pp, int req_idx) {
     if (pp->mode == 1) {
         for (int32_t p : pp->pages[req_idx]) {
             if (--pp->ref[p] == 0) pp->give_back_page(p);
+            pp->ref_changed(p);
         }
     }
     pp->pages[req_idx].clear();
@@ -340,6 +471,30 @@ extern "C" int astr_pagepool_release(astr_pagepool *pp, int req_idx) {
     for (int i = 0; i < pp->max_ctx_len; ++i) row[i] = -1;
     return ASTR_OK;
 }
+
+extern "C" int astr_pagepool_complete(astr_pagepool *pp, int req_idx, const int32_t *tokens, int n_tokens) {
+    int st = check_live(pp, req_idx);
+    if (st) return st;
+    if (n_tokens < 0 || (n_tokens > 0 && !tokens))
+        return astr::fail(ASTR_E_INVAL, "pagepool_complete: bad tokens");
+    if (n_tokens > 1) {
+        st = astr_pagepool_insert(pp, req_idx, tokens, n_tokens - 1);
+        if (st) return st;
+    }
+    return astr_pagepool_release(pp, req_idx);
+}
+
+extern "C" int64_t astr_pagepool_evict(astr_pagepool *pp, int64_t n_pages) {
+    if (!pp || n_pages < 0) {
+        astr::fail(ASTR_E_INVAL, "pagepool_evict: bad argument");
+        return -1;
+    }
+    return pp->radix_on() ? pp->evict(n_pages) : 0;
+}
+
+extern "C" int64_t astr_pagepool_cached_pages(const astr_pagepool *pp) { return pp ? pp->cached : -1; }
+
+extern "C" int64_t astr_pagepool_evicted_pages(const astr_pagepool *pp) { return pp ? pp->evicted : -1; }
 
 extern "C" const int32_t *astr_pagepool_table(const astr_pagepool *pp) {
     return pp ? pp->table.data() : nullptr;

@@ -164,6 +164,77 @@ def test_builder_lifecycle_matches_oracle():
         assert pn.p.free_pages() == sum(po.p.free)
 
 
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_builder_eviction_lifecycle_matches_oracle(seed):
+    """Random admit / extend / complete / insert / evict sequences on a pool
+    small enough that extends evict; both builders must agree on every
+    return, table, reference count and counter."""
+    _lib()
+    from paged_gqa_attention_rope_amd import AstrError, PagePool
+    rng = np.random.default_rng(seed)
+    ps, n_pages, max_reqs = 4, 32, 6
+    perm = rng.permutation(n_pages).astype(np.int32)
+    pn = PagePool(1, ps * n_pages, ps, max_reqs, 96, perm)
+    po = OraclePool(1, ps * n_pages, ps, max_reqs, 96, perm)
+    prompts = [rng.integers(0, 3, size=96).astype(np.int32) for _ in range(3)]
+    live = {}
+
+    def both(fn_n, fn_o):
+        try:
+            a = fn_n()
+        except AstrError:
+            a = "err"
+        try:
+            b = fn_o()
+        except PoolError:
+            b = "err"
+        return a, b
+
+    evictions = 0
+    for step in range(500):
+        op = rng.integers(0, 5)
+        if op <= 1 or not live:
+            toks = prompts[rng.integers(0, 3)].copy()
+            cut = int(rng.integers(0, 96))
+            toks[cut:] = rng.integers(0, 3, size=96 - cut)
+            n = int(rng.integers(1, 60))
+            a, b = both(lambda: pn.admit(toks, n), lambda: po.admit(toks, n))
+            assert a == b, (step, a, b)
+            if a == "err":
+                continue
+            r, c = a
+            ev = po.evicted
+            a, b = both(lambda: pn.extend(r, n - c), lambda: po.extend(r, n - c))
+            assert a == b, (step, a, b)
+            evictions += po.evicted > ev
+            if a == "err":
+                pn.release(r)
+                po.release(r)
+                continue
+            live[r] = (toks, n)
+        elif op == 2:
+            r = sorted(live)[rng.integers(0, len(live))]
+            toks, n = live.pop(r)
+            k = int(rng.integers(0, n + 1))        # tokens seen, the last one sampled
+            pn.complete(r, toks, k)
+            po.complete(r, toks, k)
+        elif op == 3:
+            r = sorted(live)[rng.integers(0, len(live))]
+            toks, n = live[r]
+            k = int(rng.integers(0, n + 1))
+            pn.insert(r, toks, k)
+            po.insert(r, toks, k)
+        else:
+            k = int(rng.integers(0, 5))
+            assert pn.evict(k) == po.evict(k)
+        assert np.array_equal(pn.table(), po.table), step
+        assert pn.free_pages() == po.n_free
+        assert pn.cached_pages() == po.cached_pages()
+        assert pn.evicted_pages() == po.evicted
+        assert [pn.page_ref(p) for p in range(n_pages)] == po.ref
+    assert evictions > 10
+
+
 def test_builder_errors():
     L = _lib()
     from paged_gqa_attention_rope_amd import AstrArgError, AstrError, PagePool
