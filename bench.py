@@ -55,7 +55,7 @@ TRAFFIC_JSON = os.path.join(PROFILES, "hbm_traffic.json")
 KERNEL_SOURCES = {"decode": "paged_gqa_attention_rope_amd/csrc/decode.hip",
                   "prefill": "paged_gqa_attention_rope_amd/csrc/prefill.hip"}
 # kernels (name prefixes in the rocprofv3 counter CSV) that make up each call
-CALL_KERNELS = {"decode": ("decode_mfma_kernel<128, 4>", "decode_merge_kernel<astr::bf16_t, 128>"),
+CALL_KERNELS = {"decode": ("decode_mfma_kernel<128, 4, false>", "decode_merge_kernel<astr::bf16_t, 128>"),
                 "prefill": ("prefill_mfma_kernel<128, 4, false>",)}
 
 
@@ -143,24 +143,31 @@ def cpu_baseline(cs, budget_s: float = 15.0):
 
 
 def _time_ms(fn, stream, reps: int = 10, warm: int = 2) -> float:
-    """Mean duration of fn() in ms, from HIP events on `stream`."""
+    """Mean duration of fn() in ms over `reps` back-to-back calls, from two HIP
+    events on `stream`.  A ~5 ms spin kernel goes first, so that every call
+    is queued before the first one starts and host launch time stays out of
+    the interval."""
     import torch
     for _ in range(warm):
         fn()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    evs[0].record(stream)
-    for i in range(reps):
-        fn()
-        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(10_000_000)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
-def measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream, dbytes,
-                      write_then_decode_ms):
+def measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream, dbytes):
     """The adjacent rows: the fused decode write on the decode workload, and
     the rotary gradient on a gradient of the prefill batch's q shape."""
     import paged_gqa_attention_rope_amd as astr
+    import staging
+    write_then_decode_ms = _time_ms(lambda: (staging.run_write(st_d), staging.run_decode(
+        st_d, out=out_d, o_part=o_part, lse_part=lse_part)), stream)
     fused_ms = _time_ms(lambda: astr.decode_attn_write(
         q_unrot, st_d.k, st_d.v, st_d.attn_cache, cs_d.layer_id, st_d.freqs, cs_d.split_chunk,
         out=out_d, o_part=o_part, lse_part=lse_part), stream)
@@ -336,8 +343,7 @@ def main():
     dec_gbs = dbytes / (t_dec * 1e-3) / 1e9
     pre_tfs = pflops / (t_pre * 1e-3) / 1e12
 
-    nxt = measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream, dbytes,
-                            float(t_wd + t_dec))
+    nxt = measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream, dbytes)
 
     cpu = None
     if not args.no_cpu_baseline:
