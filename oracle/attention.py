@@ -23,7 +23,9 @@ h // (n_heads / n_kv_heads); a request whose KV length L exceeds its query
 count e has a cached prefix p = L - e and its query i (0-based) sits at
 position p + i and sees keys j <= p + i; split s of a decode covers positions
 [s*C, min((s+1)*C, L)) and stores the normalised partial output and the
-natural-log log-sum-exp of its scaled scores.
+natural-log log-sum-exp of its scaled scores.  A table entry outside the
+pool names no key (the pages never produce one): that key takes no part in
+the softmax, and a query with no key left gets zeros.
 """
 
 import math
@@ -53,9 +55,11 @@ def attend(q, k, v, scale: float, mask=None) -> np.ndarray:
     s = (q @ k.T) * scale
     if mask is not None:
         s = s + mask
-    s = s - s.max(axis=1, keepdims=True)
+    mx = s.max(axis=1, keepdims=True)
+    empty = np.isneginf(mx)                      # every key masked: the row is 0
+    s = s - np.where(empty, 0.0, mx)
     p = np.exp(s)
-    p = p / p.sum(axis=1, keepdims=True)
+    p = p / np.where(empty, 1.0, p.sum(axis=1, keepdims=True))
     return p @ v
 
 
@@ -64,27 +68,36 @@ def kv_head_of(h: int, n_heads: int, n_kv_heads: int) -> int:
     return h // (n_heads // n_kv_heads)
 
 
-def decode_dense(q, k, v, scale: float) -> np.ndarray:
+def _absent(key_ok, n: int) -> np.ndarray:
+    """Additive row [n]: -inf for keys that take no part (key_ok False)."""
+    if key_ok is None:
+        return np.zeros(n)
+    return np.where(np.asarray(key_ok, dtype=bool), 0.0, -np.inf)
+
+
+def decode_dense(q, k, v, scale: float, key_ok=None) -> np.ndarray:
     """One decode query per head against a request's whole KV.
 
-    q [Hq, D], k/v [L, Hkv, D] -> [Hq, D].
+    q [Hq, D], k/v [L, Hkv, D] -> [Hq, D]; key_ok [L] (default all True).
     """
     hq, hkv = q.shape[0], k.shape[1]
+    mask = _absent(key_ok, k.shape[0])[None, :]
     out = np.empty(q.shape, dtype=np.float64)
     for h in range(hq):
         g = kv_head_of(h, hq, hkv)
-        out[h] = attend(q[h][None, :], k[:, g], v[:, g], scale)[0]
+        out[h] = attend(q[h][None, :], k[:, g], v[:, g], scale, mask)[0]
     return out
 
 
-def prefill_dense(q, k, v, scale: float) -> np.ndarray:
+def prefill_dense(q, k, v, scale: float, key_ok=None) -> np.ndarray:
     """Causal attention of e queries over a request's L = p + e keys.
 
-    q [e, Hq, D], k/v [L, Hkv, D] -> [e, Hq, D]; query i sees keys j <= p + i.
+    q [e, Hq, D], k/v [L, Hkv, D] -> [e, Hq, D]; query i sees keys j <= p + i
+    (and only keys with key_ok, default all).
     """
     e, hq, _ = q.shape
     L, hkv = k.shape[0], k.shape[1]
-    mask = causal_mask(e, L - e)
+    mask = causal_mask(e, L - e) + _absent(key_ok, L)[None, :]
     out = np.empty(q.shape, dtype=np.float64)
     for h in range(hq):
         g = kv_head_of(h, hq, hkv)
@@ -134,10 +147,15 @@ def merge_splits(o_part, lse) -> np.ndarray:
 
 # -- the paged forms: gather through req_to_token, then the dense definition ------
 
-def gather(pool, layer: int, req_to_token, req: int, length: int) -> np.ndarray:
-    """pool[layer, req_to_token[req, 0:length]] -> [length, Hkv, D]."""
-    slots = np.asarray(req_to_token)[req, :length]
-    return np.asarray(pool[layer][slots], dtype=np.float64)
+def gather(pool, layer: int, req_to_token, req: int, length: int):
+    """(pool[layer, req_to_token[req, 0:length]] -> [length, Hkv, D], key_ok
+    [length]); an entry outside the pool gathers a zero row and key_ok False."""
+    slots = np.asarray(req_to_token)[req, :length].astype(np.int64)
+    size = np.shape(pool)[1]
+    ok = (slots >= 0) & (slots < size)
+    rows = np.zeros((length,) + tuple(np.shape(pool)[2:]), dtype=np.float64)
+    rows[ok] = np.asarray(pool[layer][slots[ok]], dtype=np.float64)
+    return rows, ok
 
 
 def paged_decode(q, k_pool, v_pool, layer: int, req_to_token, req_pool_indices,
@@ -147,9 +165,9 @@ def paged_decode(q, k_pool, v_pool, layer: int, req_to_token, req_pool_indices,
     for b in range(len(req_pool_indices)):
         L = int(kv_indptr[b + 1] - kv_indptr[b])
         r = int(req_pool_indices[b])
-        k = gather(k_pool, layer, req_to_token, r, L)
-        v = gather(v_pool, layer, req_to_token, r, L)
-        out[b] = decode_dense(np.asarray(q[b], dtype=np.float64), k, v, scale)
+        k, ok = gather(k_pool, layer, req_to_token, r, L)
+        v, _ = gather(v_pool, layer, req_to_token, r, L)
+        out[b] = decode_dense(np.asarray(q[b], dtype=np.float64), k, v, scale, ok)
     return out
 
 
@@ -161,7 +179,7 @@ def paged_prefill(q, k_pool, v_pool, layer: int, req_to_token, req_pool_indices,
         q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
         L = int(kv_indptr[b + 1] - kv_indptr[b])
         r = int(req_pool_indices[b])
-        k = gather(k_pool, layer, req_to_token, r, L)
-        v = gather(v_pool, layer, req_to_token, r, L)
-        out[q0:q1] = prefill_dense(np.asarray(q[q0:q1], dtype=np.float64), k, v, scale)
+        k, ok = gather(k_pool, layer, req_to_token, r, L)
+        v, _ = gather(v_pool, layer, req_to_token, r, L)
+        out[q0:q1] = prefill_dense(np.asarray(q[q0:q1], dtype=np.float64), k, v, scale, ok)
     return out

@@ -198,3 +198,60 @@ def test_last_prefill_row_equals_decode_and_prefix_reuse():
     part = A.prefill_dense(q[p:], k, v, 0.2)
     np.testing.assert_allclose(part, full[p:], atol=1e-13)
     np.testing.assert_allclose(full[-1], A.decode_dense(q[-1], k, v, 0.2), atol=1e-13)
+
+
+def _brute_attend_or_zero(q, k, v, scale, visible):
+    """_brute_attend, but a row with no visible key is all zeros."""
+    if not any(visible(j) for j in range(len(k))):
+        return [0.0] * len(v[0])
+    return _brute_attend(q, k, v, scale, visible)
+
+
+def test_absent_keys_take_no_part_brute_force():
+    # table entries outside the pool (-1, pool size, beyond) name no key
+    rng = np.random.default_rng(19)
+    n_layers, slots, hkv, hq, d = 2, 40, 2, 4, 8
+    kp = rng.standard_normal((n_layers, slots, hkv, d))
+    vp = rng.standard_normal((n_layers, slots, hkv, d))
+    table = np.full((2, 16), -1)
+    table[0, :9] = rng.permutation(slots)[:9]
+    table[0, [1, 4]] = [-1, slots]                  # positions 1 and 4: no key
+    table[1, :3] = [slots + 3, -7, slots]           # request 1: no key at all
+    scale = 1 / math.sqrt(d)
+    ok0 = [j not in (1, 4) for j in range(9)]
+    # decode, both requests
+    q = rng.standard_normal((2, hq, d))
+    got = A.paged_decode(q, kp, vp, 1, table, [0, 1], [0, 9, 12], scale)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        k0 = [kp[1, table[0, j], g].tolist() if ok0[j] else None for j in range(9)]
+        v0 = [vp[1, table[0, j], g].tolist() if ok0[j] else [0.0] * d for j in range(9)]
+        want = _brute_attend(q[0, h], [x or [0.0] * d for x in k0], v0, scale, lambda j: ok0[j])
+        np.testing.assert_allclose(got[0, h], want, rtol=0, atol=1e-13)
+    assert np.array_equal(got[1], np.zeros((hq, d)))
+    # prefill of the last 5 tokens of request 0: causal and present
+    qq = rng.standard_normal((5, hq, d))
+    got = A.paged_prefill(qq, kp, vp, 0, table, [0], [0, 5], [0, 9], scale)
+    for i in range(5):
+        for h in range(hq):
+            g = h // (hq // hkv)
+            kk = [kp[0, table[0, j], g].tolist() if ok0[j] else [0.0] * d for j in range(9)]
+            vv = [vp[0, table[0, j], g].tolist() if ok0[j] else [0.0] * d for j in range(9)]
+            want = _brute_attend_or_zero(qq[i, h], kk, vv, scale, lambda j: ok0[j] and j <= 4 + i)
+            np.testing.assert_allclose(got[i, h], want, rtol=0, atol=1e-13)
+
+
+def test_key_mask_default_and_all_absent():
+    rng = np.random.default_rng(20)
+    q = rng.standard_normal((3, 4, 8))
+    k = rng.standard_normal((7, 2, 8))
+    v = rng.standard_normal((7, 2, 8))
+    np.testing.assert_array_equal(A.prefill_dense(q, k, v, 0.3),
+                                  A.prefill_dense(q, k, v, 0.3, np.ones(7, bool)))
+    got = A.prefill_dense(q, k, v, 0.3, np.zeros(7, bool))
+    assert np.array_equal(got, np.zeros_like(got))
+    # the first query sees keys 0..4; with those absent it gets zeros, the others do not
+    ok = np.array([False] * 5 + [True] * 2)
+    got = A.prefill_dense(q, k, v, 0.3, ok)
+    assert np.array_equal(got[0], np.zeros((4, 8)))
+    assert np.all(np.abs(got[1:]).sum(axis=-1) > 0)
