@@ -721,6 +721,441 @@ __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kern
     }
 }
 
+// ---------------------------------------------------------------------------
+// ping-pong kernel: D = 128, a multiple of 4 query heads per KV head
+// ---------------------------------------------------------------------------
+// On gfx950 a wave's matrix-core products and its vector ALU work do not
+// overlap, but those of two waves sharing a SIMD do, provided one is in its
+// matrix-core phase while the other is in its vector phase (measured: a
+// product stream next to an ALU stream of half its length costs about as much
+// as the product stream alone; two waves running the same mixed stream in
+// step cost more than the two run one after the other).  So one workgroup of
+// 8 waves takes a query tile and 4 query heads of a KV head: waves 0-3
+// (group A) hold heads 0-1 and waves 4-7 (group B) heads 2-3 of the same 64
+// rows, and the hardware places waves w and w+4 on one SIMD.  Every wave
+// alternates
+//   VALU(s): LDS reads of K(s+1); mask, running max and P(s) =
+//            exp2(S(s) - m); slot indices and row copies for later steps;
+//   MFMA(s): LDS reads of V(s) (they land while the next products run);
+//            S(s+1) = K(s+1) Q^T and O^T += V(s)^T P(s)^T (+ row sums);
+// and group B runs one phase behind group A, with a workgroup barrier at the
+// end of every phase: while A multiplies, B forms probabilities, and the
+// other way round.  Keys arrive through a ring of 6 LDS slots by
+// asynchronous copies issued 4 steps ahead (slot indices 6 steps ahead), so
+// copies have at least 5 phases to land; all waits are explicit counts.
+// Step t's slot is read from K(t)'s read in VALU(t-1) (group A) to V(t)'s in
+// MFMA(t) (group B), i.e. phases 2t-1 .. 2t+3; step t+6 is copied into it
+// from VALU(t+2) on, phase 2t+5 or later.
+// Measured against prefill_mfma_kernel: about 5% faster on 64 requests of
+// 2048 cached + 64 new tokens, level (within run-to-run noise) on 16 requests
+// with radix prefixes, where one workgroup per CU leaves a longer tail.  A
+// step still takes about twice its matrix-core time: the vector phase (about
+// 150 instructions, issued one per cycle slot next to the other wave's
+// products), not the products, sets the pace.
+
+// Keep a value's computation before this point: an empty asm that reads and
+// rewrites the registers (volatile asm statements keep their order, and the
+// phase barriers are volatile asm).
+__device__ __forceinline__ void pin(Frag8 &x) { asm volatile("" : "+v"(x.v)); }
+__device__ __forceinline__ void pin(f32x4_t &x) { asm volatile("" : "+v"(x)); }
+template <typename T, int N>
+__device__ __forceinline__ void pin(T (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) pin(x[i]);
+}
+
+struct PpCfg {
+    static constexpr int D = 128, TQ = 64, HW = 2, WAVES = 8, THREADS = 64 * WAVES;
+    static constexpr int TS = 32, NB = 6, NI = 8;     // keys per step, ring slots, index slots
+    static constexpr int KS = D / 32, DB = D / 16, SL = D / 8, RB = 2 * D, MAT = TS * RB;
+    static constexpr int SLOT = 2 * MAT;               // one step's K rows, then its V rows
+    static constexpr int RPI = 1024 / RB;              // rows one wave-wide 16-byte copy fills
+    static_assert(RPI * WAVES == TS, "one K and one V copy per wave and step");
+};
+
+template <int G, bool WIDE>
+__global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
+    const uint16_t *__restrict__ q, uint16_t *__restrict__ out, const uint16_t *__restrict__ k_layer,
+    const uint16_t *__restrict__ v_layer, int64_t pool_slots, int n_kv,
+    const int32_t *__restrict__ req_to_token, int num_reqs, int max_ctx_len,
+    const int32_t *__restrict__ req_pool_indices, const int32_t *__restrict__ qo_indptr,
+    const int32_t *__restrict__ kv_indptr, const int32_t *__restrict__ q_tile_to_batch,
+    const int32_t *__restrict__ q_tile_to_index, int batch, int total_q, int n_heads,
+    int num_q_tiles, float scale_log2) {
+    using C = PpCfg;
+    constexpr int D = C::D, TQ = C::TQ, HW = C::HW, KS = C::KS, DB = C::DB, SL = C::SL, RB = C::RB;
+    constexpr int MAT = C::MAT, SLOT = C::SLOT, TS = C::TS, NB = C::NB, NI = C::NI, RPI = C::RPI;
+    constexpr int WAVES = C::WAVES;
+    constexpr int GROUPS = G / 4;                      // workgroups per KV head
+    constexpr float kLazy = 8.f;
+    static_assert(G % 4 == 0, "4 query heads per workgroup");
+
+    // tiles dealt to the 8 XCDs heaviest first, as in prefill_mfma_kernel
+    const int units_per_tile = n_kv * GROUPS;
+    const int xcd = blockIdx.x % kXcds, k_in = blockIdx.x / kXcds;
+    const int tile = kXcds * (k_in / units_per_tile) + xcd;
+    if (tile >= num_q_tiles) return;
+    const int u = k_in % units_per_tile;
+    const int kvh = u / GROUPS;
+    const int hg = u % GROUPS;
+    TileInfo ti;
+    if (!tile_info(tile, q_tile_to_batch, q_tile_to_index, qo_indptr, kv_indptr,
+                   req_pool_indices, batch, num_reqs, max_ctx_len, total_q, TQ, ti))
+        return;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool grp_b = wave >= 4;                      // group B: one phase behind
+    const int g = lane >> 4, j = lane & 15;
+    const int r0 = 16 * (wave & 3);                    // first tile row of this wave
+    const int h0 = kvh * G + 4 * hg + 2 * (wave >> 2); // first query head of this wave
+    const int qpos0 = ti.p + ti.row0 + r0;
+    const int qpos = qpos0 + j;
+    const int nsteps = (ti.kv_end + TS - 1) / TS;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NB * SLOT];
+    auto slot_ptr = [&](auto rc) -> uint8_t * {
+        constexpr int R = decltype(rc)::value;
+        return ring + R * SLOT;
+    };
+    __shared__ int32_t sidx[NI][WAVES][RPI];          // slot indices of a step's rows
+    __shared__ uint32_t badw[NB][2];                   // per step: a byte per wave, bit r: row 4w+r missing
+
+    Frag8 qf[HW][KS];
+    {
+        int r = r0 + j;
+        if (r >= ti.rows) r = 0;
+        const uint16_t *src = q + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h0) * D + 8 * g;
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[hh][ks].u = *reinterpret_cast<const uint4 *>(src + hh * D + 32 * ks);
+        }
+    }
+    f32x4_t o[HW][DB], osum[HW];
+    float m[HW], neg_m[HW], thr[HW];
+    const float inv_scale = 1.f / scale_log2;
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+        m[hh] = -INFINITY;
+        neg_m[hh] = 0.f;
+        thr[hh] = -INFINITY;
+        osum[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[hh][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    Frag8 ones;
+    ones.u = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+
+    uint32_t kofs[KS], vofs[DB];
+    {
+        const uint32_t kb0 = RB * j + 16 * (g ^ swz<D>(j));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kofs[ks] = kb0 ^ (64 * ks);
+        const int vr = 4 * g + (j >> 2);
+        const uint32_t vb0 = RB * vr + 8 * (j & 1) + 16 * (((j & 3) >> 1) ^ swz<D>(vr));
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vofs[db] = vb0 ^ (32 * db);
+    }
+
+    // copies: wave w fills rows 4w .. 4w+3 of a step (lane l: row 4w + l/16,
+    // chunk position l % 16, reading chunk (l % 16) ^ swz(row))
+    const int crow = RPI * wave + lane / SL;
+    const uint32_t ccol = (WIDE ? 0 : kvh * RB) + 16 * ((lane % SL) ^ swz<D>(crow));
+    const int32_t *trow = req_to_token + static_cast<int64_t>(ti.req) * max_ctx_len;
+    const uint32_t slot_lim = static_cast<uint32_t>(min(pool_slots, static_cast<int64_t>(INT32_MAX)));
+    const uint32_t stride = WIDE ? RB : static_cast<uint32_t>(n_kv) * RB;
+    const uint32_t records = WIDE ? static_cast<uint32_t>(min(static_cast<int64_t>(slot_lim) * n_kv,
+                                                              static_cast<int64_t>(UINT32_MAX)))
+                                  : slot_lim;
+    const i32x4_t krs = buffer_rsrc(k_layer, stride, records);
+    const i32x4_t vrs = buffer_rsrc(v_layer, stride, records);
+    const i32x4_t trs = buffer_rsrc(trow, 0, 4u * static_cast<uint32_t>(ti.kv_end));
+    const uint32_t idx_voff = 4u * (RPI * wave + lane);
+    const uint32_t sidx_base = lds_addr(sidx) + 4u * RPI * wave;
+
+    // slot indices of step t's rows 4w .. 4w+3 into index slot t % NI
+    auto fetch_idx = [&](int t) {
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(4u * TS * t);
+        asm volatile("" : : "s"(soff));
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(sidx_base + 4u * RPI * WAVES * (t & (NI - 1)));
+        if (lane < RPI) copy_raw4_to_lds(trs, idx_voff, soff, dst);
+    };
+    // this lane's row's slot index of step t (its index copy has landed)
+    auto slot_index = [&](int t) -> int32_t { return sidx[t & (NI - 1)][wave][lane / SL]; };
+    // rows of step t into ring slot R (t >= nsteps, or past the visible keys:
+    // out-of-range records, which read zeros; the copy count never changes)
+    auto issue = [&](auto rc, int t, int32_t sl) {
+        constexpr int R = decltype(rc)::value;
+        const bool ok = static_cast<uint32_t>(sl) < slot_lim;
+        uint32_t rec;
+        if constexpr (WIDE) rec = ok ? static_cast<uint32_t>(sl) * n_kv + kvh : 0xffffffffu;
+        else rec = static_cast<uint32_t>(sl);
+        if (crow >= ti.kv_end - TS * t) rec = 0xffffffffu;
+        const uint32_t dk = lds_addr(slot_ptr(rc)) + RB * RPI * wave;
+        copy_record16_to_lds(krs, rec, ccol, dk);
+        copy_record16_to_lds(vrs, rec, ccol, dk + MAT);
+        uint32_t byte = 0;
+        if (__builtin_expect(__any(!ok), 0)) {
+            const uint64_t b = __ballot(!ok);
+#pragma unroll
+            for (int r = 0; r < RPI; ++r)
+                if ((b >> (r * SL)) & 1u) byte |= 1u << r;
+        }
+        if (lane == 0) reinterpret_cast<uint8_t *>(badw[R])[wave] = static_cast<uint8_t>(byte);
+    };
+    auto load_k = [&](auto rc, Frag8 (&kf)[KS][2]) {
+        const uint8_t *base = slot_ptr(rc);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                kf[ks][kb].u = *reinterpret_cast<const uint4 *>(base + 16 * RB * kb + kofs[ks]);
+        }
+    };
+    auto load_v = [&](auto rc, Frag8 (&vf)[DB]) {
+        const uint8_t *vbase = slot_ptr(rc) + MAT;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            vf[db].h[0] = lds_read_tr16(reinterpret_cast<const uint16_t *>(vbase + vofs[db]));
+            vf[db].h[1] = lds_read_tr16(reinterpret_cast<const uint16_t *>(vbase + 16 * RB + vofs[db]));
+        }
+    };
+    auto qk = [&](const Frag8 (&kf)[KS][2], f32x4_t (&sc)[HW][2]) {
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+            sc[hh][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            sc[hh][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int hh = 0; hh < HW; ++hh) sc[hh][kb] = mfma16(kf[ks][kb], qf[hh][ks], sc[hh][kb]);
+            }
+        }
+    };
+    auto probs = [&](const f32x4_t (&sc)[HW][2], Frag8 (&pf)[HW]) {
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+            float p[2][4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p[kb][r] = __builtin_amdgcn_exp2f(fmaf(sc[hh][kb][r], scale_log2, neg_m[hh]));
+            }
+            pf[hh].w[0] = cvt_pk_bf16(p[0][0], p[0][1]);
+            pf[hh].w[1] = cvt_pk_bf16(p[0][2], p[0][3]);
+            pf[hh].w[2] = cvt_pk_bf16(p[1][0], p[1][1]);
+            pf[hh].w[3] = cvt_pk_bf16(p[1][2], p[1][3]);
+        }
+    };
+    auto pv = [&](const Frag8 (&vf)[DB], const Frag8 (&pf)[HW]) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) o[hh][db] = mfma16(vf[db], pf[hh], o[hh][db]);
+        }
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) osum[hh] = mfma16(ones, pf[hh], osum[hh]);
+    };
+    auto local_max = [&](const f32x4_t (&sc)[HW][2], float (&lm)[HW]) {
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh)
+            lm[hh] = fmaxf(fmaxf(fmaxf(sc[hh][0][0], sc[hh][0][1]), fmaxf(sc[hh][0][2], sc[hh][0][3])),
+                           fmaxf(fmaxf(sc[hh][1][0], sc[hh][1][1]), fmaxf(sc[hh][1][2], sc[hh][1][3])));
+    };
+    auto apply_mask = [&](f32x4_t (&sc)[HW][2], int kb0, uint32_t okw) {
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int k = 16 * kb + 4 * g + r;
+                    if (!((okw >> k) & 1u) || kb0 + k > qpos) sc[hh][kb][r] = -INFINITY;
+                }
+            }
+        }
+    };
+    // Raise the running max where a score exceeds it by more than kLazy (as
+    // in prefill_mfma_kernel); returns whether the accumulators must be
+    // rescaled by alpha, which the next matrix-core phase does before its
+    // products (so the accumulators are only ever touched in that phase).
+    auto update_max = [&](const float (&lm)[HW], float (&alpha)[HW]) -> bool {
+        bool fire = false;
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) fire = fire || lm[hh] > thr[hh];
+        if (__builtin_expect(!__any(fire), 1)) return false;
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+            const float mx = max_over_groups(lm[hh]) * scale_log2;
+            const float mnew = mx > m[hh] + kLazy ? mx : m[hh];
+            alpha[hh] = exp2_sub(m[hh], mnew);
+            m[hh] = mnew;
+            neg_m[hh] = mnew == -INFINITY ? 0.f : -mnew;
+            thr[hh] = (mnew + kLazy) * inv_scale;
+        }
+        return true;
+    };
+    auto rescale = [&](const float (&alpha)[HW]) {
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+            osum[hh] *= alpha[hh];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[hh][db] *= alpha[hh];
+        }
+    };
+    // keys of a step whose slot lies in the pool, from its per-wave bytes
+    // d0, d1 (bit 4w + r <- wave w's bit r)
+    auto ok_mask = [&](uint32_t d0, uint32_t d1) -> uint32_t {
+        if (__builtin_expect((d0 | d1) == 0, 1)) return 0xffffffffu;
+        uint32_t bits = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            bits |= ((d0 >> (8 * w)) & 0xfu) << (RPI * w);
+            bits |= ((d1 >> (8 * w)) & 0xfu) << (RPI * (w + 4));
+        }
+        return ~bits;
+    };
+    // a phase ends: this wave's LDS traffic is complete, then all waves meet;
+    // no instruction moves across it
+    auto phase_end = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Copy bookkeeping: each VALU(s) issues 3 copies, the indices of step
+    // s+6 then the K and V rows of step s+4.  Step t's rows must land by the
+    // end of phase 2t-2 (K(t) is first read in phase 2t-1), which falls in
+    // MFMA(t-2) for group A and in VALU(t-2) for group B; there each wave
+    // waits for the copies of step s+2 with s = t-2: 6 copies were issued
+    // after them (5 when s = 0, after the prologue's order).
+    auto wait_rows = [&](int s) {
+        if (s == 0) wait_copies<5>();
+        else wait_copies<6>();
+    };
+
+    // prologue: indices of steps 0..5, rows of steps 0..3 (each index copy
+    // waited for by the count of copies issued after it)
+    for (int t = 0; t < 6; ++t) fetch_idx(t);
+    wait_copies<5>();
+    issue(int_c<0>{}, 0, slot_index(0));
+    wait_copies<6>();
+    issue(int_c<1>{}, 1, slot_index(1));
+    wait_copies<7>();
+    issue(int_c<2>{}, 2, slot_index(2));
+    wait_copies<8>();
+    issue(int_c<3>{}, 3, slot_index(3));
+    wait_copies<6>();                                  // rows of step 0
+    phase_end();
+    if (grp_b) {                                       // B: idle first phase
+        wait_copies<4>();                              // rows of step 1
+        phase_end();
+    }
+    f32x4_t sc[HW][2];
+    {
+        Frag8 kf[KS][2];
+        load_k(int_c<0>{}, kf);
+        __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0)
+        qk(kf, sc);
+        pin(sc);
+    }
+    if (!grp_b) wait_copies<4>();                      // A: rows of step 1
+    phase_end();
+
+    // step 0's missing-slot bytes (written in the prologue, published by its barrier)
+    uint32_t bad_d0 = __builtin_amdgcn_readfirstlane(static_cast<int>(badw[0][0]));
+    uint32_t bad_d1 = __builtin_amdgcn_readfirstlane(static_cast<int>(badw[0][1]));
+    // one step: VALU(s), then MFMA(s); true after the last one
+    auto step = [&](auto rc, int s) -> bool {
+        constexpr int R = decltype(rc)::value;
+        constexpr int R1 = (R + 1) % NB, R4 = (R + 4) % NB;
+        const bool more = s + 1 < nsteps;
+        // the small LDS reads first (LDS reads complete in order, so nothing
+        // below waits for the K operands): the slot indices of step s+4, whose
+        // copy has landed (5 copies were issued after it), and this step's
+        // missing-slot bytes; then the K operands of step s+1
+        // this phase runs at raised issue priority, so that its vector work
+        // goes first and the other wave's matrix-core products fill the gaps
+        // (measured: a few percent faster than raising the products instead)
+        __builtin_amdgcn_s_setprio(1);
+        wait_copies<5>();
+        const int32_t sl4 = slot_index(s + 4);
+        // the next step's missing-slot bytes (written in VALU(s-3)), kept in
+        // scalar registers for VALU(s+1), so that no phase waits for them
+        const uint32_t nd0 = badw[R1][0], nd1 = badw[R1][1];
+        const uint32_t d0 = bad_d0, d1 = bad_d1;
+        // (K is read unconditionally, so that the compiler's count of
+        // outstanding LDS reads stays exact; after the last step it goes unused)
+        Frag8 kf[KS][2], vf[DB], pf[HW];
+        load_k(int_c<R1>{}, kf);
+        float alpha[HW];
+        bool resc;
+        {
+            float lm[HW];
+            local_max(sc, lm);
+            const uint32_t okw = ok_mask(d0, d1);
+            const int kb0 = TS * s;
+            if (kb0 + TS - 1 > qpos0 || okw != 0xffffffffu) {
+                apply_mask(sc, kb0, okw);
+                local_max(sc, lm);
+            }
+            resc = update_max(lm, alpha);
+        }
+        probs(sc, pf);
+        pin(pf);                                       // P(s) is formed in this phase
+        fetch_idx(s + 6);
+        issue(int_c<R4>{}, s + 4, sl4);
+        bad_d0 = __builtin_amdgcn_readfirstlane(static_cast<int>(nd0));
+        bad_d1 = __builtin_amdgcn_readfirstlane(static_cast<int>(nd1));
+        __builtin_amdgcn_s_setprio(0);
+        if (grp_b) wait_rows(s);
+        phase_end();
+        load_v(rc, vf);
+        if (__builtin_expect(resc, 0)) rescale(alpha);
+        if (more) {
+            qk(kf, sc);
+            pin(sc);                                   // S(s+1) is formed in this phase
+        }
+        pv(vf, pf);
+        pin(o);
+        pin(osum);
+        if (!grp_b) wait_rows(s);
+        phase_end();
+        return !more;
+    };
+    for (int s = 0;; s += NB) {
+        if (step(int_c<0>{}, s)) break;
+        if (step(int_c<1>{}, s + 1)) break;
+        if (step(int_c<2>{}, s + 2)) break;
+        if (step(int_c<3>{}, s + 3)) break;
+        if (step(int_c<4>{}, s + 4)) break;
+        if (step(int_c<5>{}, s + 5)) break;
+    }
+    if (!grp_b) phase_end();                           // A: idle last phase
+    wait_copies<0>();
+
+    const int r = r0 + j;
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+        const float ls = osum[hh][0];
+        if (r >= ti.rows) continue;
+        const float inv = ls > 0.f ? 1.f / ls : 0.f;
+        uint16_t *dst = out + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h0 + hh) * D + 4 * g;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            uint2 w;
+            w.x = cvt_pk_bf16(o[hh][db][0] * inv, o[hh][db][1] * inv);
+            w.y = cvt_pk_bf16(o[hh][db][2] * inv, o[hh][db][3] * inv);
+            *reinterpret_cast<uint2 *>(dst + 16 * db) = w;
+        }
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_generic(const PrefillArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((prefill_generic_kernel<T, D>), dim3(a.num_q_tiles, a.n_heads), dim3(256), 0, s,
@@ -747,8 +1182,29 @@ hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int G, bool WIDE>
+hipError_t launch_pp(const PrefillArgs &a, hipStream_t s) {
+    const int64_t units = static_cast<int64_t>((a.num_q_tiles + kXcds - 1) / kXcds) * kXcds *
+                          a.pool.n_kv_heads * (G / 4);
+    hipLaunchKernelGGL((prefill_pp_kernel<G, WIDE>), dim3(static_cast<unsigned>(units)), dim3(PpCfg::THREADS),
+                       0, s, static_cast<const uint16_t *>(a.q), static_cast<uint16_t *>(a.out),
+                       static_cast<const uint16_t *>(a.pool.k_layer),
+                       static_cast<const uint16_t *>(a.pool.v_layer), a.pool.pool_slots,
+                       a.pool.n_kv_heads, a.req_to_token, a.num_reqs, a.max_ctx_len, a.req_pool_indices,
+                       a.qo_indptr, a.kv_indptr, a.q_tile_to_batch, a.q_tile_to_index, a.batch,
+                       a.total_q, a.n_heads, a.num_q_tiles, a.scale_log2);
+    return hipGetLastError();
+}
+
 template <int D, bool WIDE>
 hipError_t launch_mfma_g(const PrefillArgs &a, hipStream_t s) {
+    if constexpr (D == 128) {
+        switch (a.n_heads / a.pool.n_kv_heads) {
+            case 4: return launch_pp<4, WIDE>(a, s);
+            case 8: return launch_pp<8, WIDE>(a, s);
+            default: break;
+        }
+    }
     switch (a.n_heads / a.pool.n_kv_heads) {
         case 1: return launch_mfma<D, 1, WIDE>(a, s);
         case 2: return launch_mfma<D, 2, WIDE>(a, s);

@@ -64,27 +64,31 @@ def request_kv(cs, b: int, k_rot: np.ndarray):
     return (np.concatenate([kh.astype(np.float64), kn]), np.concatenate([vh.astype(np.float64), vn]))
 
 
-def expected_decode(cs, sample=None, rot=None):
-    """{b: [Hq, D]} for the newest token of each sampled request."""
+def expected_decode(cs, sample=None, rot=None, key_ok=None):
+    """{b: [Hq, D]} for the newest token of each sampled request (key_ok:
+    {b: bool [L_b]} marks the keys that take part, default all)."""
     q_rot, k_rot = rot if rot is not None else rotated_new(cs)
     off = new_offsets(cs)
     scale = 1.0 / math.sqrt(cs.head_dim)
     out = {}
     for b in (range(cs.batch) if sample is None else sample):
         K, V = request_kv(cs, b, k_rot)
-        out[b] = A.decode_dense(q_rot[off[b + 1] - 1], K, V, scale)
+        ok = None if key_ok is None else key_ok.get(b)
+        out[b] = A.decode_dense(q_rot[off[b + 1] - 1], K, V, scale, ok)
     return out
 
 
-def expected_prefill(cs, sample=None, rot=None):
-    """{b: [e_b, Hq, D]} for the new rows of each sampled request."""
+def expected_prefill(cs, sample=None, rot=None, key_ok=None):
+    """{b: [e_b, Hq, D]} for the new rows of each sampled request (key_ok as
+    for expected_decode)."""
     q_rot, k_rot = rot if rot is not None else rotated_new(cs)
     off = new_offsets(cs)
     scale = 1.0 / math.sqrt(cs.head_dim)
     out = {}
     for b in (range(cs.batch) if sample is None else sample):
         K, V = request_kv(cs, b, k_rot)
-        out[b] = A.prefill_dense(q_rot[off[b]:off[b + 1]], K, V, scale)
+        ok = None if key_ok is None else key_ok.get(b)
+        out[b] = A.prefill_dense(q_rot[off[b]:off[b + 1]], K, V, scale, ok)
     return out
 
 

@@ -96,6 +96,10 @@ PREFILL = {
     "wide-slot-g1-kv64-d128": lambda: _pre(28, batch=3, n_heads=64, n_kv_heads=64, mode=1,
                                            page_size=16, pool_slots=4096, n_groups=2,
                                            prefix_pages_hi=6, ext_lo=20, ext_hi=90, max_ctx_len=200),
+    # 4 query heads per KV head with slots wider than a record stride
+    "wide-slot-g4-kv64-d128": lambda: _pre(29, batch=2, n_heads=256, n_kv_heads=64, mode=1,
+                                           page_size=16, pool_slots=2048, n_groups=2,
+                                           prefix_pages_hi=4, ext_lo=30, ext_hi=70, max_ctx_len=160),
     "prefix-f32-d64": lambda: _pre(27, head_dim=64, dtype="f32", mode=1, page_size=16,
                                    pool_slots=8192, n_groups=2, prefix_pages_hi=10, ext_hi=90,
                                    max_ctx_len=260),
@@ -331,6 +335,58 @@ def test_prefill_parity(name):
     off = E.new_offsets(cs)
     for b in range(cs.batch):
         E.assert_close(got[off[b]:off[b + 1]], want[b], cs.dtype, f"{name} request {b}")
+
+
+def _corrupt_table(st, cs, rng, per_request=6):
+    """Point some table entries of every request outside the pool; returns
+    {b: bool [L_b]} of the keys that still take part."""
+    bad_values = [-1, cs.pool_slots, cs.pool_slots + 4097, 2 ** 31 - 1]
+    t = st.attn_cache.req_to_token
+    key_ok = {}
+    for b, r in enumerate(st.reqs):
+        L = int(cs.seq_lens[b])
+        ok = np.ones(L, dtype=bool)
+        if b == 0 and L <= 40:
+            ok[:] = False                        # a request with no key left at all
+        else:
+            pos = rng.choice(L, size=min(per_request, L - 1), replace=False)
+            ok[pos] = False
+        for j in np.nonzero(~ok)[0]:
+            t[r, int(j)] = int(bad_values[int(j) % len(bad_values)])
+        key_ok[b] = ok
+    return key_ok
+
+
+@pytest.mark.parametrize("name", ["cfg4", "ragged-65-129", "tiny-extends", "prefix-g8-d128",
+                                  "prefix-g6-d64", "prefix-page16-g1-d64", "prefix-f32-d64"])
+def test_prefill_keys_outside_pool_take_no_part(name):
+    cs = PREFILL[name]()
+    say(f"prefill with table entries outside the pool, case={name} seed={cs.seed}")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    key_ok = _corrupt_table(st, cs, np.random.default_rng(cs.seed + 7))
+    out = staging.run_prefill(st)
+    torch.cuda.synchronize()
+    want = E.expected_prefill(cs, key_ok=key_ok)
+    got = to_np(out)
+    off = E.new_offsets(cs)
+    for b in range(cs.batch):
+        E.assert_close(got[off[b]:off[b + 1]], want[b], cs.dtype, f"{name} request {b}")
+
+
+@pytest.mark.parametrize("name", ["cfg2", "g8-d128", "g6-d64", "g2-d128-f32", "length-one-and-two"])
+def test_decode_keys_outside_pool_take_no_part(name):
+    cs = DECODE[name]()
+    say(f"decode with table entries outside the pool, case={name} seed={cs.seed}")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    key_ok = _corrupt_table(st, cs, np.random.default_rng(cs.seed + 7))
+    out = staging.run_decode(st)
+    torch.cuda.synchronize()
+    want = E.expected_decode(cs, key_ok=key_ok)
+    got = to_np(out)
+    for b in range(cs.batch):
+        E.assert_close(got[b], want[b], cs.dtype, f"{name} request {b}")
 
 
 @pytest.mark.parametrize("name", ["cfg4", "prefix-g6-d64", "prefix-f32-d64"])
