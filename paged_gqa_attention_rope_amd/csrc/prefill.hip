@@ -735,7 +735,7 @@ __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kern
 // rows, and the hardware places waves w and w+4 on one SIMD.  Every wave
 // alternates
 //   VALU(s): LDS reads of K(s+1); mask, running max and P(s) =
-//            exp2(S(s) - m); slot indices and row copies for later steps;
+//            exp2(S(s)); slot indices and row copies for later steps;
 //   MFMA(s): LDS reads of V(s) (they land while the next products run);
 //            S(s+1) = K(s+1) Q^T and O^T += V(s)^T P(s)^T (+ row sums);
 // and group B runs one phase behind group A, with a workgroup barrier at the
@@ -746,12 +746,22 @@ __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kern
 // Step t's slot is read from K(t)'s read in VALU(t-1) (group A) to V(t)'s in
 // MFMA(t) (group B), i.e. phases 2t-1 .. 2t+3; step t+6 is copied into it
 // from VALU(t+2) on, phase 2t+5 or later.
-// Measured against prefill_mfma_kernel: about 5% faster on 64 requests of
-// 2048 cached + 64 new tokens, level (within run-to-run noise) on 16 requests
-// with radix prefixes, where one workgroup per CU leaves a longer tail.  A
-// step still takes about twice its matrix-core time: the vector phase (about
-// 150 instructions, issued one per cycle slot next to the other wave's
-// products), not the products, sets the pace.
+// The vector phase is kept short:
+//  * Q is multiplied by scale*log2(e) and rounded to bf16 once, when it is
+//    loaded, and every score accumulator starts at -m (the running max), so
+//    the products deliver the exponent itself and P needs only the exp2 and
+//    the bf16 packing.  The extra rounding of Q adds a relative error of at
+//    most 2^-9 per element of q; on the radix-prefix batch the relative L2
+//    error against the float64 definition goes from 2.4e-3 to 2.9e-3.
+//  * The keys of a step whose slot lies outside the pool are found by one
+//    ballot over the step's 32 slot indices, read from the index ring a
+//    phase ahead; no per-wave flags are written.
+//  * The raise test of the running max is one ballot per head.
+// Measured against prefill_mfma_kernel: about 15% faster on 64 requests of
+// 2048 cached + 64 new tokens, about 5% on 16 requests with radix prefixes,
+// whose time is set by the longest tile (one workgroup per CU).  Moving the
+// maxima or the probabilities into the matrix-core phase, or reading V there
+// in the vector phase instead, was measured slower or level.
 
 // Keep a value's computation before this point: an empty asm that reads and
 // rewrites the registers (volatile asm statements keep their order, and the
@@ -805,7 +815,7 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool grp_b = wave >= 4;                      // group B: one phase behind
+    const int grp_b = __builtin_amdgcn_readfirstlane(wave >= 4 ? 1 : 0);   // group B: one phase behind
     const int g = lane >> 4, j = lane & 15;
     const int r0 = 16 * (wave & 3);                    // first tile row of this wave
     const int h0 = kvh * G + 4 * hg + 2 * (wave >> 2); // first query head of this wave
@@ -819,7 +829,6 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         return ring + R * SLOT;
     };
     __shared__ int32_t sidx[NI][WAVES][RPI];          // slot indices of a step's rows
-    __shared__ uint32_t badw[NB][2];                   // per step: a byte per wave, bit r: row 4w+r missing
 
     Frag8 qf[HW][KS];
     {
@@ -829,18 +838,30 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qf[hh][ks].u = *reinterpret_cast<const uint4 *>(src + hh * D + 32 * ks);
+            for (int ks = 0; ks < KS; ++ks) {
+                Frag8 raw;
+                raw.u = *reinterpret_cast<const uint4 *>(src + hh * D + 32 * ks);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = __uint_as_float(raw.w[e] << 16) * scale_log2;
+                    const float hi = __uint_as_float(raw.w[e] & 0xffff0000u) * scale_log2;
+                    qf[hh][ks].w[e] = cvt_pk_bf16(lo, hi);
+                }
+            }
         }
     }
     f32x4_t o[HW][DB], osum[HW];
+    // m: running row max (log2 domain); bias = -m (0 while nothing is
+    // visible) starts each score accumulator, so a product's result is
+    // already the exponent; thr: accumulator value above which m is raised
     float m[HW], neg_m[HW], thr[HW];
-    const float inv_scale = 1.f / scale_log2;
+    f32x4_t bias[HW];
 #pragma unroll
     for (int hh = 0; hh < HW; ++hh) {
         m[hh] = -INFINITY;
         neg_m[hh] = 0.f;
         thr[hh] = -INFINITY;
+        bias[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         osum[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[hh][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -896,14 +917,14 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         const uint32_t dk = lds_addr(slot_ptr(rc)) + RB * RPI * wave;
         copy_record16_to_lds(krs, rec, ccol, dk);
         copy_record16_to_lds(vrs, rec, ccol, dk + MAT);
-        uint32_t byte = 0;
-        if (__builtin_expect(__any(!ok), 0)) {
-            const uint64_t b = __ballot(!ok);
-#pragma unroll
-            for (int r = 0; r < RPI; ++r)
-                if ((b >> (r * SL)) & 1u) byte |= 1u << r;
-        }
-        if (lane == 0) reinterpret_cast<uint8_t *>(badw[R])[wave] = static_cast<uint8_t>(byte);
+    };
+    // bit k: key k of step t has its slot in the pool.  The 32 slot indices
+    // of a step lie contiguously in its index slot (wave w's 4 rows at 4w);
+    // every wave's index copy of step t landed (and was waited for) before it
+    // issued its rows of t, several barriers ago.
+    auto idx_of_step = [&](int t) -> int32_t { return (&sidx[t & (NI - 1)][0][0])[lane & 31]; };
+    auto ok_bits = [&](int32_t ix) -> uint32_t {
+        return static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(static_cast<uint32_t>(ix) < slot_lim));
     };
     auto load_k = [&](auto rc, Frag8 (&kf)[KS][2]) {
         const uint8_t *base = slot_ptr(rc);
@@ -924,16 +945,12 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     };
     auto qk = [&](const Frag8 (&kf)[KS][2], f32x4_t (&sc)[HW][2]) {
 #pragma unroll
-        for (int hh = 0; hh < HW; ++hh) {
-            sc[hh][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            sc[hh][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int hh = 0; hh < HW; ++hh) sc[hh][kb] = mfma16(kf[ks][kb], qf[hh][ks], sc[hh][kb]);
+                for (int hh = 0; hh < HW; ++hh)
+                    sc[hh][kb] = mfma16(kf[ks][kb], qf[hh][ks], ks == 0 ? bias[hh] : sc[hh][kb]);
             }
         }
     };
@@ -944,8 +961,7 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    p[kb][r] = __builtin_amdgcn_exp2f(fmaf(sc[hh][kb][r], scale_log2, neg_m[hh]));
+                for (int r = 0; r < 4; ++r) p[kb][r] = __builtin_amdgcn_exp2f(sc[hh][kb][r]);
             }
             pf[hh].w[0] = cvt_pk_bf16(p[0][0], p[0][1]);
             pf[hh].w[1] = cvt_pk_bf16(p[0][2], p[0][3]);
@@ -968,7 +984,7 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
             lm[hh] = fmaxf(fmaxf(fmaxf(sc[hh][0][0], sc[hh][0][1]), fmaxf(sc[hh][0][2], sc[hh][0][3])),
                            fmaxf(fmaxf(sc[hh][1][0], sc[hh][1][1]), fmaxf(sc[hh][1][2], sc[hh][1][3])));
     };
-    auto apply_mask = [&](f32x4_t (&sc)[HW][2], int kb0, uint32_t okw) {
+    auto apply_mask = [&](f32x4_t (&sc)[HW][2], int kb0, uint32_t okw) __attribute__((always_inline)) {
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
 #pragma unroll
@@ -985,19 +1001,29 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     // in prefill_mfma_kernel); returns whether the accumulators must be
     // rescaled by alpha, which the next matrix-core phase does before its
     // products (so the accumulators are only ever touched in that phase).
-    auto update_max = [&](const float (&lm)[HW], float (&alpha)[HW]) -> bool {
-        bool fire = false;
+    auto update_max = [&](const float (&lm)[HW], float (&alpha)[HW], f32x4_t (&sc)[HW][2]) -> bool {
+        uint64_t fire = 0;
 #pragma unroll
-        for (int hh = 0; hh < HW; ++hh) fire = fire || lm[hh] > thr[hh];
-        if (__builtin_expect(!__any(fire), 1)) return false;
+        for (int hh = 0; hh < HW; ++hh) fire |= __builtin_amdgcn_ballot_w64(lm[hh] > thr[hh]);
+        if (__builtin_expect(fire == 0, 1)) return false;
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
-            const float mx = max_over_groups(lm[hh]) * scale_log2;
+            const float mx = max_over_groups(lm[hh]) - neg_m[hh];       // the row max, log2 domain
             const float mnew = mx > m[hh] + kLazy ? mx : m[hh];
             alpha[hh] = exp2_sub(m[hh], mnew);
             m[hh] = mnew;
-            neg_m[hh] = mnew == -INFINITY ? 0.f : -mnew;
-            thr[hh] = (mnew + kLazy) * inv_scale;
+            const float nb = mnew == -INFINITY ? 0.f : -mnew;
+            const float shift = nb - neg_m[hh];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sc[hh][kb] += shift;
+            neg_m[hh] = nb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {                // in place: no copies on the common path
+                float x = bias[hh][r];
+                asm volatile("v_mov_b32 %0, %1" : "+v"(x) : "v"(nb));
+                bias[hh][r] = x;
+            }
+            thr[hh] = mnew == -INFINITY ? -INFINITY : kLazy;
         }
         return true;
     };
@@ -1011,16 +1037,6 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     };
     // keys of a step whose slot lies in the pool, from its per-wave bytes
     // d0, d1 (bit 4w + r <- wave w's bit r)
-    auto ok_mask = [&](uint32_t d0, uint32_t d1) -> uint32_t {
-        if (__builtin_expect((d0 | d1) == 0, 1)) return 0xffffffffu;
-        uint32_t bits = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            bits |= ((d0 >> (8 * w)) & 0xfu) << (RPI * w);
-            bits |= ((d1 >> (8 * w)) & 0xfu) << (RPI * (w + 4));
-        }
-        return ~bits;
-    };
     // a phase ends: this wave's LDS traffic is complete, then all waves meet;
     // no instruction moves across it
     auto phase_end = [&]() {
@@ -1067,9 +1083,10 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     if (!grp_b) wait_copies<4>();                      // A: rows of step 1
     phase_end();
 
-    // step 0's missing-slot bytes (written in the prologue, published by its barrier)
-    uint32_t bad_d0 = __builtin_amdgcn_readfirstlane(static_cast<int>(badw[0][0]));
-    uint32_t bad_d1 = __builtin_amdgcn_readfirstlane(static_cast<int>(badw[0][1]));
+    // keys of step 0 with a slot in the pool (its indices landed in the prologue)
+    uint32_t okw_cur = ok_bits(idx_of_step(0));
+    // first step whose keys cross the causal diagonal of this wave's first row
+    const int s_diag = (qpos0 + 1) / TS;
     // one step: VALU(s), then MFMA(s); true after the last one
     auto step = [&](auto rc, int s) -> bool {
         constexpr int R = decltype(rc)::value;
@@ -1077,18 +1094,18 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         const bool more = s + 1 < nsteps;
         // the small LDS reads first (LDS reads complete in order, so nothing
         // below waits for the K operands): the slot indices of step s+4, whose
-        // copy has landed (5 copies were issued after it), and this step's
-        // missing-slot bytes; then the K operands of step s+1
+        // copy has landed (5 copies were issued after it), and the 32 slot
+        // indices of step s+1; then the K operands of step s+1
         // this phase runs at raised issue priority, so that its vector work
         // goes first and the other wave's matrix-core products fill the gaps
         // (measured: a few percent faster than raising the products instead)
         __builtin_amdgcn_s_setprio(1);
         wait_copies<5>();
         const int32_t sl4 = slot_index(s + 4);
-        // the next step's missing-slot bytes (written in VALU(s-3)), kept in
-        // scalar registers for VALU(s+1), so that no phase waits for them
-        const uint32_t nd0 = badw[R1][0], nd1 = badw[R1][1];
-        const uint32_t d0 = bad_d0, d1 = bad_d1;
+        // step s+1's keys with a slot in the pool, as a scalar mask for
+        // VALU(s+1), so that no phase waits for the read
+        const int32_t nix = idx_of_step(s + 1);
+        const uint32_t okw = okw_cur;
         // (K is read unconditionally, so that the compiler's count of
         // outstanding LDS reads stays exact; after the last step it goes unused)
         Frag8 kf[KS][2], vf[DB], pf[HW];
@@ -1097,21 +1114,15 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         bool resc;
         {
             float lm[HW];
+            if (__builtin_expect(s >= s_diag || okw != 0xffffffffu, 0)) apply_mask(sc, TS * s, okw);
             local_max(sc, lm);
-            const uint32_t okw = ok_mask(d0, d1);
-            const int kb0 = TS * s;
-            if (kb0 + TS - 1 > qpos0 || okw != 0xffffffffu) {
-                apply_mask(sc, kb0, okw);
-                local_max(sc, lm);
-            }
-            resc = update_max(lm, alpha);
+            resc = update_max(lm, alpha, sc);
         }
         probs(sc, pf);
         pin(pf);                                       // P(s) is formed in this phase
         fetch_idx(s + 6);
         issue(int_c<R4>{}, s + 4, sl4);
-        bad_d0 = __builtin_amdgcn_readfirstlane(static_cast<int>(nd0));
-        bad_d1 = __builtin_amdgcn_readfirstlane(static_cast<int>(nd1));
+        okw_cur = ok_bits(nix);
         __builtin_amdgcn_s_setprio(0);
         if (grp_b) wait_rows(s);
         phase_end();
