@@ -868,6 +868,7 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     }
     Frag8 ones;
     ones.u = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+    pin(ones);                                         // a register, not rematerialised each step
 
     uint32_t kofs[KS], vofs[DB];
     {
@@ -999,8 +1000,9 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     };
     // Raise the running max where a score exceeds it by more than kLazy (as
     // in prefill_mfma_kernel); returns whether the accumulators must be
-    // rescaled by alpha, which the next matrix-core phase does before its
-    // products (so the accumulators are only ever touched in that phase).
+    // rescaled by alpha.  The caller rescales at once, on this rare path (it
+    // waits for the last products of the accumulators), so that no branch
+    // remains in the matrix-core phase.
     auto update_max = [&](const float (&lm)[HW], float (&alpha)[HW], f32x4_t (&sc)[HW][2]) -> bool {
         uint64_t fire = 0;
 #pragma unroll
@@ -1047,29 +1049,28 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     // Copy bookkeeping: each VALU(s) issues 3 copies, the indices of step
     // s+6 then the K and V rows of step s+4.  Step t's rows must land by the
     // end of phase 2t-2 (K(t) is first read in phase 2t-1), which falls in
-    // MFMA(t-2) for group A and in VALU(t-2) for group B; there each wave
-    // waits for the copies of step s+2 with s = t-2: 6 copies were issued
-    // after them (5 when s = 0, after the prologue's order).
-    auto wait_rows = [&](int s) {
-        if (s == 0) wait_copies<5>();
-        else wait_copies<6>();
-    };
-
-    // prologue: indices of steps 0..5, rows of steps 0..3 (each index copy
-    // waited for by the count of copies issued after it)
-    for (int t = 0; t < 6; ++t) fetch_idx(t);
-    wait_copies<5>();
+    // MFMA(t-2) for group A and in VALU(t-2) for group B.  Every wave waits
+    // for them at the end of its VALU(t-2), when 6 copies have been issued
+    // after them (for group A one phase earlier than needed, which costs
+    // nothing measurable and keeps every wait a constant count).
+    // prologue: indices of steps 0..5, rows of steps 0..3, in the order
+    // that puts exactly 6 copies after the rows of step 2 by the end of
+    // VALU(0), as in every later step (each index copy waited for by the
+    // count of copies issued after it)
+    for (int t = 0; t < 5; ++t) fetch_idx(t);
+    wait_copies<4>();
     issue(int_c<0>{}, 0, slot_index(0));
-    wait_copies<6>();
+    wait_copies<5>();
     issue(int_c<1>{}, 1, slot_index(1));
-    wait_copies<7>();
+    wait_copies<6>();
     issue(int_c<2>{}, 2, slot_index(2));
+    fetch_idx(5);
     wait_copies<8>();
     issue(int_c<3>{}, 3, slot_index(3));
-    wait_copies<6>();                                  // rows of step 0
+    wait_copies<7>();                                  // rows of step 0
     phase_end();
     if (grp_b) {                                       // B: idle first phase
-        wait_copies<4>();                              // rows of step 1
+        wait_copies<5>();                              // rows of step 1
         phase_end();
     }
     f32x4_t sc[HW][2];
@@ -1080,7 +1081,7 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         qk(kf, sc);
         pin(sc);
     }
-    if (!grp_b) wait_copies<4>();                      // A: rows of step 1
+    if (!grp_b) wait_copies<5>();                      // A: rows of step 1
     phase_end();
 
     // keys of step 0 with a slot in the pool (its indices landed in the prologue)
@@ -1096,10 +1097,6 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         // below waits for the K operands): the slot indices of step s+4, whose
         // copy has landed (5 copies were issued after it), and the 32 slot
         // indices of step s+1; then the K operands of step s+1
-        // this phase runs at raised issue priority, so that its vector work
-        // goes first and the other wave's matrix-core products fill the gaps
-        // (measured: a few percent faster than raising the products instead)
-        __builtin_amdgcn_s_setprio(1);
         wait_copies<5>();
         const int32_t sl4 = slot_index(s + 4);
         // step s+1's keys with a slot in the pool, as a scalar mask for
@@ -1110,24 +1107,22 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         // outstanding LDS reads stays exact; after the last step it goes unused)
         Frag8 kf[KS][2], vf[DB], pf[HW];
         load_k(int_c<R1>{}, kf);
-        float alpha[HW];
-        bool resc;
         {
-            float lm[HW];
+            float lm[HW], alpha[HW];
             if (__builtin_expect(s >= s_diag || okw != 0xffffffffu, 0)) apply_mask(sc, TS * s, okw);
             local_max(sc, lm);
-            resc = update_max(lm, alpha, sc);
+            if (__builtin_expect(update_max(lm, alpha, sc), 0)) rescale(alpha);
         }
         probs(sc, pf);
         pin(pf);                                       // P(s) is formed in this phase
         fetch_idx(s + 6);
         issue(int_c<R4>{}, s + 4, sl4);
         okw_cur = ok_bits(nix);
-        __builtin_amdgcn_s_setprio(0);
-        if (grp_b) wait_rows(s);
+        // rows of step s+2 (6 copies were issued after them): group B reads
+        // K(s+2) in its next phase; group A only after its MFMA(s)
+        wait_copies<6>();
         phase_end();
         load_v(rc, vf);
-        if (__builtin_expect(resc, 0)) rescale(alpha);
         if (more) {
             qk(kf, sc);
             pin(sc);                                   // S(s+1) is formed in this phase
@@ -1135,7 +1130,6 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         pv(vf, pf);
         pin(o);
         pin(osum);
-        if (!grp_b) wait_rows(s);
         phase_end();
         return !more;
     };
