@@ -82,6 +82,15 @@ typedef struct astr_kv_meta {
     int32_t max_len;                  /* host: max KV length over the batch */
     int32_t num_q_tiles;              /* host (prefill) */
     int32_t q_tile;                   /* host (prefill): query rows per tile */
+    /* Decode work items (optional).  When set, the decode calls launch one
+     * workgroup per (item, KV head) instead of one per (batch entry, split
+     * index below ceil(max_len / split_chunk)), most of which would find
+     * their split past the request's end and exit without work.  Built by
+     * astr_decode_split_items for the split_chunk of the call. */
+    const int32_t *split_item_batch;  /* [num_split_items]: batch entry of each item */
+    const int32_t *split_item_index;  /* [num_split_items]: split index of each item */
+    int32_t num_split_items;          /* host: 0 = no item list */
+    int32_t split_item_chunk;         /* host: split_chunk the items were built for */
 } astr_kv_meta;
 
 /* Message for the last non-OK status returned on the calling thread. */
@@ -157,6 +166,26 @@ int astr_rope_backward(void *grad, const int32_t *positions, int n_tokens, int n
 
 /* Number of KV splits S = ceil(max_len / split_chunk) (0 on bad input). */
 int astr_decode_num_splits(int max_len, int split_chunk);
+/*
+ * The decode work items of a step (host only): for each batch entry b the
+ * splits s < max(1, ceil(seq_lens[b] / split_chunk)) -- every (request,
+ * split) that holds keys, the partials of the KVCache record's
+ * decode_o_part / decode_ml_part (inference.md, "KVCache System"), and split
+ * 0 of an empty request, whose output is zero.  Full splits come first in
+ * batch order, then each entry's last split, longest first (ties by batch
+ * entry), so that the shortest work is dispatched last.
+ *   seq_lens    host [batch], KV length of each batch entry
+ *   item_batch  host [capacity], written: batch entry of each item
+ *   item_index  host [capacity], written: split index of each item
+ *   *num_items  the number of items written
+ * The decode calls use the list when astr_kv_meta.split_item_batch is set;
+ * it must list every split of every entry, as built here (a split left out
+ * is neither computed nor merged correctly).
+ * Errors: INVAL (null pointer, batch < 0, split_chunk < 1, a negative
+ * length, capacity short).
+ */
+int astr_decode_split_items(const int32_t *seq_lens, int batch, int split_chunk, int32_t *item_batch,
+                            int32_t *item_index, int capacity, int *num_items);
 
 /*
  * o[b, h] = sum_j softmax_j(q[b, h] . K_j * sm_scale) V_j over the KV
@@ -180,7 +209,10 @@ int astr_decode_num_splits(int max_len, int split_chunk);
  *   lse_part  device [batch, n_heads, S] float32 scratch
  *   m         host; uses the pool fields, req_to_token, num_reqs, max_ctx_len,
  *             req_pool_indices, kv_indptr, batch, max_len (>= every L_b;
- *             it sizes the split axis and the grid)
+ *             it sizes the split axis and, without work items, the grid),
+ *             and the decode work items when split_item_batch is set
+ *             (then split_item_index, num_split_items >= 1 and
+ *             split_item_chunk == split_chunk are required)
  * Requests with L_b == 0 get a zero output.  Errors: INVAL, UNSUPPORTED, LAUNCH.
  */
 int astr_decode_attn(const void *q, void *out, int n_heads, const astr_kv_meta *m,

@@ -17,7 +17,7 @@ ASTR_BF16 = 1
 # every symbol include/astr.h declares
 EXPORTS = (
     "astr_last_error", "astr_rope_table", "astr_rope_kv_write", "astr_rope_backward",
-    "astr_decode_num_splits", "astr_decode_attn_write",
+    "astr_decode_num_splits", "astr_decode_split_items", "astr_decode_attn_write",
     "astr_decode_attn", "astr_prefill_attn", "astr_pagepool_create", "astr_pagepool_destroy",
     "astr_pagepool_admit", "astr_pagepool_extend", "astr_pagepool_bind", "astr_pagepool_insert",
     "astr_pagepool_release", "astr_pagepool_table", "astr_pagepool_free_pages",
@@ -39,6 +39,8 @@ class KvMeta(ctypes.Structure):
         ("q_tile_to_batch", c_vp), ("q_tile_to_index", c_vp),
         ("batch", ctypes.c_int32), ("max_len", ctypes.c_int32),
         ("num_q_tiles", ctypes.c_int32), ("q_tile", ctypes.c_int32),
+        ("split_item_batch", c_vp), ("split_item_index", c_vp),
+        ("num_split_items", ctypes.c_int32), ("split_item_chunk", ctypes.c_int32),
     ]
 
 
@@ -60,6 +62,7 @@ def lib():
                                      ctypes.POINTER(KvMeta), c_int, c_vp]
     L.astr_rope_backward.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_vp, c_int, c_int, c_vp]
     L.astr_decode_num_splits.argtypes = [c_int, c_int]
+    L.astr_decode_split_items.argtypes = [c_i32p, c_int, c_int, c_i32p, c_i32p, c_int, ctypes.POINTER(c_int)]
     L.astr_decode_attn.argtypes = [c_vp, c_vp, c_int, ctypes.POINTER(KvMeta), c_int, c_int,
                                    ctypes.c_float, c_vp, c_vp, c_vp]
     L.astr_decode_attn_write.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, ctypes.POINTER(KvMeta), c_int, c_vp,

@@ -71,24 +71,49 @@ class KVCache:
     q_tile_to_index: Optional[torch.Tensor] = None
     num_q_tiles: int = 0
     q_tile: int = 64
+    # decode work items (batch entry, split) for split_item_chunk; optional
+    split_item_batch: Optional[torch.Tensor] = None
+    split_item_index: Optional[torch.Tensor] = None
+    num_split_items: int = 0
+    split_item_chunk: int = 0
 
     @property
     def batch(self) -> int:
         return int(self.req_pool_indices.numel())
 
 
+def decode_split_items(seq_lens, split_chunk: int):
+    """Host (batch entry, split) work items of a decode step
+    (astr_decode_split_items); returns two int32 arrays."""
+    seq = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    _need(split_chunk >= 1, "split_chunk must be positive")
+    cap = int(sum(max(1, -(-int(x) // split_chunk)) for x in seq))
+    ib = np.zeros(max(cap, 1), np.int32)
+    ix = np.zeros(max(cap, 1), np.int32)
+    n = ctypes.c_int()
+    check(lib().astr_decode_split_items(_i32p(seq), int(seq.size), int(split_chunk), _i32p(ib), _i32p(ix),
+                                        max(cap, 1), ctypes.byref(n)))
+    return ib[:n.value], ix[:n.value]
+
+
 def cache_from_bind(k_buffer: torch.Tensor, v_buffer: torch.Tensor, table: np.ndarray,
-                    meta: dict) -> KVCache:
-    """Upload one step's host metadata (PagePool.bind) next to the pool."""
+                    meta: dict, split_chunk: Optional[int] = None) -> KVCache:
+    """Upload one step's host metadata (PagePool.bind) next to the pool; with
+    split_chunk, also the decode work items for that chunk."""
     dev = k_buffer.device
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
-    return KVCache(k_buffer=k_buffer, v_buffer=v_buffer, req_to_token=up(table),
-                   req_pool_indices=up(meta["req_pool_indices"]), seq_lens=up(meta["seq_lens"]),
-                   out_cache_loc=up(meta["out_cache_loc"]), kv_indptr=up(meta["kv_indptr"]),
-                   max_len=int(meta["max_len"]), qo_indptr=up(meta["qo_indptr"]),
-                   q_tile_to_batch=up(meta["q_tile_to_batch"]),
-                   q_tile_to_index=up(meta["q_tile_to_index"]),
-                   num_q_tiles=int(meta["num_q_tiles"]), q_tile=int(meta["q_tile"]))
+    c = KVCache(k_buffer=k_buffer, v_buffer=v_buffer, req_to_token=up(table),
+                req_pool_indices=up(meta["req_pool_indices"]), seq_lens=up(meta["seq_lens"]),
+                out_cache_loc=up(meta["out_cache_loc"]), kv_indptr=up(meta["kv_indptr"]),
+                max_len=int(meta["max_len"]), qo_indptr=up(meta["qo_indptr"]),
+                q_tile_to_batch=up(meta["q_tile_to_batch"]),
+                q_tile_to_index=up(meta["q_tile_to_index"]),
+                num_q_tiles=int(meta["num_q_tiles"]), q_tile=int(meta["q_tile"]))
+    if split_chunk is not None:
+        ib, ix = decode_split_items(meta["seq_lens"], split_chunk)
+        c.split_item_batch, c.split_item_index = up(ib), up(ix)
+        c.num_split_items, c.split_item_chunk = int(ib.size), int(split_chunk)
+    return c
 
 
 def _meta(c: KVCache, need_prefill: bool = False) -> KvMeta:
@@ -111,6 +136,12 @@ def _meta(c: KVCache, need_prefill: bool = False) -> KvMeta:
     m.req_pool_indices = c.req_pool_indices.data_ptr()
     m.kv_indptr = c.kv_indptr.data_ptr()
     m.batch, m.max_len = b, int(c.max_len)
+    if c.num_split_items > 0:
+        _dev_tensor(c.split_item_batch, "split_item_batch", torch.int32, kb.device, c.num_split_items)
+        _dev_tensor(c.split_item_index, "split_item_index", torch.int32, kb.device, c.num_split_items)
+        m.split_item_batch = c.split_item_batch.data_ptr()
+        m.split_item_index = c.split_item_index.data_ptr()
+        m.num_split_items, m.split_item_chunk = int(c.num_split_items), int(c.split_item_chunk)
     if need_prefill:
         _dev_tensor(c.qo_indptr, "qo_indptr", torch.int32, kb.device, b + 1)
         _dev_tensor(c.q_tile_to_batch, "q_tile_to_batch", torch.int32, kb.device, c.num_q_tiles)

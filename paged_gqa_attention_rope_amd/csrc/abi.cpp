@@ -166,6 +166,18 @@ int decode_args(const char *what, const void *q, void *out, int n_heads, const a
         return fail(ASTR_E_INVAL, "%s: %d splits need o_part and lse_part", what, ns);
     if (static_cast<int64_t>(m->batch) * ns * m->n_kv_heads > INT32_MAX)
         return fail(ASTR_E_UNSUPPORTED, "%s: grid too large", what);
+    if (m->split_item_batch || m->split_item_index || m->num_split_items) {
+        if (!m->split_item_batch || !m->split_item_index || m->num_split_items < 1)
+            return fail(ASTR_E_INVAL, "%s: incomplete decode work items", what);
+        if (m->split_item_chunk != split_chunk)
+            return fail(ASTR_E_INVAL, "%s: work items built for split_chunk %d, called with %d", what,
+                        m->split_item_chunk, split_chunk);
+        if (static_cast<int64_t>(m->num_split_items) * m->n_kv_heads > INT32_MAX)
+            return fail(ASTR_E_UNSUPPORTED, "%s: grid too large", what);
+        a.item_batch = m->split_item_batch;
+        a.item_index = m->split_item_index;
+        a.num_items = m->num_split_items;
+    }
     a.q = q;
     a.out = out;
     a.o_part = o_part;

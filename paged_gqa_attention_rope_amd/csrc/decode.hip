@@ -7,8 +7,12 @@
 // k/v_buffer[layer, slot, kv_head, :]; split-K writes partial outputs and
 // max/log-sum partials that a second pass merges.
 //
-// Pass 1, one workgroup per (request b, KV head, split s): the split's KV
-// positions are streamed once.  Each 16-byte slice of a KV row is read by one
+// Pass 1, one workgroup per (request b, KV head, split s) -- per (work item,
+// KV head) when the step's list of (request, split) items is given, else per
+// (request, split below ceil(max_len / C), KV head), where the splits past a
+// request's end exit at once (on a batch of mixed lengths most of that grid;
+// launching them costs the dispatcher more time than their work).  The
+// split's KV positions are streamed once.  Each 16-byte slice of a KV row is read by one
 // lane; a row (head_dim elements) is read by D/E consecutive lanes, so every
 // wave-wide load is a run of whole 256-byte (bf16, D=128) row segments.  All
 // G query heads of the KV head consume each row from registers, so the pool is
@@ -31,6 +35,24 @@ namespace {
 
 constexpr float kLn2 = 0.693147180559945309f;
 
+// The (KV head, split, batch entry) of this workgroup: from the work-item
+// list when there is one (a workgroup per (item, KV head)), else from the
+// full (entry, split, KV head) grid.  False for an item outside the batch or
+// the split axis (skipped, never dereferenced).
+__device__ __forceinline__ bool work_item(const int32_t *item_batch, const int32_t *item_index, int num_items,
+                                          int batch, int n_kv, int n_splits, int &kvh, int &s, int &b) {
+    kvh = blockIdx.x % n_kv;
+    if (num_items > 0) {
+        const int item = blockIdx.x / n_kv;
+        b = item_batch[item];
+        s = item_index[item];
+        return b >= 0 && b < batch && s >= 0 && s < n_splits;
+    }
+    s = (blockIdx.x / n_kv) % n_splits;
+    b = blockIdx.x / (n_kv * n_splits);
+    return true;
+}
+
 template <typename T, int D, int G>
 struct DecodeCfg {
     static constexpr int E = Vec<T>::N;          // elements per lane per row
@@ -48,13 +70,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     float *__restrict__ lse_part, const T *__restrict__ k_layer, const T *__restrict__ v_layer,
     int64_t pool_slots, int n_kv, const int32_t *__restrict__ req_to_token, int num_reqs,
     int max_ctx_len, const int32_t *__restrict__ req_pool_indices,
-    const int32_t *__restrict__ kv_indptr, int n_heads, int chunk, int n_splits, float scale_log2) {
+    const int32_t *__restrict__ kv_indptr, int n_heads, int chunk, int n_splits, float scale_log2,
+    const int32_t *__restrict__ item_batch, const int32_t *__restrict__ item_index, int num_items, int batch) {
     using C = DecodeCfg<T, D, G>;
     constexpr int E = C::E, LPR = C::LPR, NRG = C::NRG, U = C::U;
 
-    const int kvh = blockIdx.x % n_kv;
-    const int s = (blockIdx.x / n_kv) % n_splits;
-    const int b = blockIdx.x / (n_kv * n_splits);
+    int kvh, s, b;
+    if (!work_item(item_batch, item_index, num_items, batch, n_kv, n_splits, kvh, s, b)) return;
     const int req = req_pool_indices[b];
     const int L = request_len(kv_indptr, b, req, num_reqs, min(max_ctx_len, n_splits * chunk));
     const int start = s * chunk;
@@ -240,7 +262,8 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
     const int32_t *__restrict__ req_pool_indices, const int32_t *__restrict__ kv_indptr,
     int n_heads, int chunk, int n_splits, float scale_log2, const uint16_t *__restrict__ k_new,
     const uint16_t *__restrict__ v_new, const float2 *__restrict__ tab, int max_pos, uint16_t *k_store,
-    uint16_t *v_store) {
+    uint16_t *v_store, const int32_t *__restrict__ item_batch, const int32_t *__restrict__ item_index,
+    int num_items, int batch) {
     constexpr int KS = D / 32;          // k-steps of S^T
     constexpr int DB = D / 16;          // 16-row blocks of O^T
     constexpr int CK = 32;              // keys per wave chunk
@@ -248,9 +271,8 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
     constexpr int WAVES = 4;
     static_assert(G <= 16, "query heads per KV head must fit the 16 MFMA columns");
 
-    const int kvh = blockIdx.x % n_kv;
-    const int s = (blockIdx.x / n_kv) % n_splits;
-    const int b = blockIdx.x / (n_kv * n_splits);
+    int kvh, s, b;
+    if (!work_item(item_batch, item_index, num_items, batch, n_kv, n_splits, kvh, s, b)) return;
     const int req = req_pool_indices[b];
     const int L = request_len(kv_indptr, b, req, num_reqs, min(max_ctx_len, n_splits * chunk));
     const int start = s * chunk;
@@ -522,7 +544,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 template <typename T, int D, int G>
 hipError_t launch_decode_typed(const DecodeArgs &a, hipStream_t s) {
     const int n_kv = a.pool.n_kv_heads;
-    const int64_t blocks = static_cast<int64_t>(a.batch) * a.n_splits * n_kv;
+    const int64_t blocks = a.num_items > 0 ? static_cast<int64_t>(a.num_items) * n_kv
+                                           : static_cast<int64_t>(a.batch) * a.n_splits * n_kv;
     if constexpr (sizeof(T) == 2) {
         auto kern = a.k_new ? decode_mfma_kernel<D, G, true> : decode_mfma_kernel<D, G, false>;
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
@@ -533,14 +556,15 @@ hipError_t launch_decode_typed(const DecodeArgs &a, hipStream_t s) {
                            a.n_heads, a.split_chunk, a.n_splits, a.scale_log2,
                            static_cast<const uint16_t *>(a.k_new), static_cast<const uint16_t *>(a.v_new),
                            reinterpret_cast<const float2 *>(a.freqs), a.max_pos,
-                           static_cast<uint16_t *>(a.pool.k_layer), static_cast<uint16_t *>(a.pool.v_layer));
+                           static_cast<uint16_t *>(a.pool.k_layer), static_cast<uint16_t *>(a.pool.v_layer),
+                           a.item_batch, a.item_index, a.num_items, a.batch);
     } else {
         hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                            s, static_cast<const T *>(a.q), static_cast<T *>(a.out), a.o_part, a.lse_part,
                            static_cast<const T *>(a.pool.k_layer), static_cast<const T *>(a.pool.v_layer),
                            a.pool.pool_slots, n_kv, a.req_to_token, a.num_reqs, a.max_ctx_len,
                            a.req_pool_indices, a.kv_indptr, a.n_heads, a.split_chunk, a.n_splits,
-                           a.scale_log2);
+                           a.scale_log2, a.item_batch, a.item_index, a.num_items, a.batch);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_splits == 1) return e;

@@ -45,6 +45,10 @@ struct DecodeArgs {
     int split_chunk;
     int n_splits;
     float scale_log2;       // sm_scale * log2(e)
+    // work items (batch entry, split); num_items == 0: one slot per (entry, split)
+    const int32_t *item_batch;
+    const int32_t *item_index;
+    int num_items;
     // fused rotary write of the step's new token (null k_new: plain decode)
     const void *k_new;
     const void *v_new;

@@ -508,3 +508,44 @@ extern "C" int astr_pagepool_page_ref(const astr_pagepool *pp, int64_t logical_p
     if (!pp || logical_page < 0 || logical_page >= pp->n_pages) return -1;
     return pp->ref[logical_page];
 }
+
+extern "C" int astr_decode_split_items(const int32_t *seq_lens, int batch, int split_chunk, int32_t *item_batch,
+                                       int32_t *item_index, int capacity, int *num_items) {
+    if (!seq_lens || !num_items || batch < 0 || split_chunk < 1 || capacity < 0 ||
+        (capacity > 0 && (!item_batch || !item_index)))
+        return astr::fail(ASTR_E_INVAL, "decode_split_items: bad argument");
+    int64_t total = 0;
+    for (int b = 0; b < batch; ++b) {
+        if (seq_lens[b] < 0) return astr::fail(ASTR_E_INVAL, "decode_split_items: seq_lens[%d] < 0", b);
+        total += std::max<int64_t>(1, (static_cast<int64_t>(seq_lens[b]) + split_chunk - 1) / split_chunk);
+    }
+    if (total > capacity)
+        return astr::fail(ASTR_E_INVAL, "decode_split_items: %lld items, capacity %d",
+                          static_cast<long long>(total), capacity);
+    // full splits (every split but the last) in batch order
+    int n = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int ns = std::max(1, (seq_lens[b] + split_chunk - 1) / split_chunk);
+        for (int s = 0; s + 1 < ns; ++s) {
+            item_batch[n] = b;
+            item_index[n] = s;
+            ++n;
+        }
+    }
+    // each entry's last split, longest first, ties by batch entry
+    std::vector<std::pair<int, int>> last;      // (-length of the last split, b)
+    last.reserve(batch);
+    for (int b = 0; b < batch; ++b) {
+        const int ns = std::max(1, (seq_lens[b] + split_chunk - 1) / split_chunk);
+        last.emplace_back(-(seq_lens[b] - (ns - 1) * split_chunk), b);
+    }
+    std::sort(last.begin(), last.end());
+    for (const auto &e : last) {
+        const int b = e.second;
+        item_batch[n] = b;
+        item_index[n] = std::max(1, (seq_lens[b] + split_chunk - 1) / split_chunk) - 1;
+        ++n;
+    }
+    *num_items = n;
+    return ASTR_OK;
+}

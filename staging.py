@@ -119,7 +119,7 @@ def stage(cs: Case, device="cuda", canary: bool = True, threads: int = 16) -> St
     if cs.kind == "decode":
         ameta = pp.bind(reqs, np.ones(cs.batch, dtype=np.int32), 64)
         st.attn_meta = ameta
-        st.attn_cache = astr.cache_from_bind(k_buffer, v_buffer, table, ameta)
+        st.attn_cache = astr.cache_from_bind(k_buffer, v_buffer, table, ameta, split_chunk=cs.split_chunk)
         last = wmeta["qo_indptr"][1:] - 1
         st.q_index = _to_dev(last.astype(np.int64), torch.int64, dev)
     else:

@@ -220,6 +220,32 @@ def test_decode_parity(name):
         E.assert_close(got[b], want[b], cs.dtype, f"{name} request {b} (L={cs.seq_lens[b]})")
 
 
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "g2-d128-f32", "g8-d128"])
+def test_decode_work_items_equal_full_grid(name):
+    """The work-item grid (one workgroup per split that holds keys) gives the
+    same bits as the full (entry, split) grid, also with the items listed in
+    another order."""
+    cs = DECODE[name]()
+    say(f"decode work items case={name} B={cs.batch} C={cs.split_chunk}")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    q = staging.decode_query(st)
+    c = st.attn_cache
+    assert c.num_split_items > 0
+    full = astr.KVCache(**{**c.__dict__, "split_item_batch": None, "split_item_index": None,
+                           "num_split_items": 0, "split_item_chunk": 0})
+    perm = torch.randperm(c.num_split_items, generator=torch.Generator().manual_seed(3)).to(q.device)
+    shuf = astr.KVCache(**{**c.__dict__, "split_item_batch": c.split_item_batch[perm].contiguous(),
+                           "split_item_index": c.split_item_index[perm].contiguous()})
+    outs = [astr.decode_attn(q, cc, cs.layer_id, cs.split_chunk) for cc in (c, full, shuf)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    want = E.expected_decode(cs)
+    got = to_np(outs[0])
+    for b in range(cs.batch):
+        E.assert_close(got[b], want[b], cs.dtype, f"{name} request {b}")
+
+
 FUSED = [n for n in DECODE if n not in ("cfg1", "g2-d128-f32", "g4-d64-f32-page1")]   # bf16, one new token each
 
 

@@ -310,3 +310,61 @@ def test_attention_calls_validate_before_launch():
     assert so.astr_decode_num_splits(0, 256) == 1
     assert so.astr_decode_num_splits(10, 0) == 0
     assert b"rope_backward: n_tokens -1" in so.astr_last_error()
+
+
+def _items_rule(lens, chunk):
+    """The decode work items stated as a rule: every split of every entry
+    (split 0 for an empty one); full splits in batch order, then the last
+    splits, longest first, ties by batch entry."""
+    ns = [max(1, -(-int(x) // chunk)) for x in lens]
+    full = [(b, s) for b in range(len(lens)) for s in range(ns[b] - 1)]
+    last = sorted(range(len(lens)), key=lambda b: (-(int(lens[b]) - (ns[b] - 1) * chunk), b))
+    return full + [(b, ns[b] - 1) for b in last]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_split_items_follow_the_rule(seed):
+    import paged_gqa_attention_rope_amd as astr
+    _lib()
+    rng = np.random.default_rng(seed)
+    lens = np.concatenate([rng.integers(0, 3000, size=40), [0, 1, 512, 513, 1024]]).astype(np.int32)
+    for chunk in (1, 7, 256, 512, 4096):
+        ib, ix = astr.decode_split_items(lens, chunk)
+        got = list(zip(ib.tolist(), ix.tolist()))
+        assert got == _items_rule(lens, chunk), chunk
+        # each (entry, split) once, and exactly the splits that hold keys (split 0 always)
+        assert len(set(got)) == len(got)
+        assert sorted(got) == sorted((b, s) for b in range(lens.size)
+                                     for s in range(max(1, -(-int(lens[b]) // chunk))))
+
+
+def test_decode_split_items_errors_and_abi_checks():
+    import paged_gqa_attention_rope_amd as astr
+    L = _lib()
+    so = L.lib()
+    with pytest.raises(Exception):
+        astr.decode_split_items(np.array([5, -1], np.int32), 4)
+    seq = np.array([10, 20], np.int32)
+    ib = np.zeros(2, np.int32)
+    n = ctypes.c_int()
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert so.astr_decode_split_items(p(seq), 2, 8, p(ib), p(ib), 2, ctypes.byref(n)) == L.ASTR_E_INVAL  # needs 5
+    assert so.astr_decode_split_items(p(seq), 2, 0, p(ib), p(ib), 8, ctypes.byref(n)) == L.ASTR_E_INVAL
+    assert so.astr_decode_split_items(p(seq), 0, 8, None, None, 0, ctypes.byref(n)) == L.ASTR_OK
+    assert n.value == 0
+    # the decode calls check the work items before anything is launched
+    m = L.KvMeta()
+    m.k_buffer = m.v_buffer = 0x1000
+    m.pool_slots, m.n_layers, m.n_kv_heads, m.head_dim, m.kv_dtype = 64, 2, 2, 128, L.ASTR_BF16
+    m.req_to_token = m.req_pool_indices = m.kv_indptr = 0x4000
+    m.num_reqs, m.max_ctx_len, m.batch, m.max_len = 1, 8, 1, 8
+    q = ctypes.c_void_p(0x2000)
+    m.split_item_batch = 0x5000                          # index list missing
+    m.num_split_items, m.split_item_chunk = 1, 64
+    assert so.astr_decode_attn(q, q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, None) == L.ASTR_E_INVAL
+    m.split_item_index = 0x6000
+    m.split_item_chunk = 32                              # built for another chunk
+    assert so.astr_decode_attn(q, q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, None) == L.ASTR_E_INVAL
+    assert b"split_chunk 32" in so.astr_last_error()
+    m.split_item_chunk, m.num_split_items = 64, 0        # no count
+    assert so.astr_decode_attn(q, q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, None) == L.ASTR_E_INVAL
