@@ -91,6 +91,22 @@ typedef struct astr_kv_meta {
     const int32_t *split_item_index;  /* [num_split_items]: split index of each item */
     int32_t num_split_items;          /* host: 0 = no item list */
     int32_t split_item_chunk;         /* host: split_chunk the items were built for */
+    /* Prefill work plan (optional; built by astr_prefill_plan).  A unit is a
+     * query tile's key steps [step_lo, step_hi) (steps of 32 keys; step_hi is
+     * clamped to the tile's last step).  When set, the bf16 prefill with
+     * head_dim 128 and a multiple of 4 query heads per KV head launches one
+     * workgroup per (unit, KV head, group of 4 query heads), in unit order;
+     * other configurations ignore the plan.  The two units of a split tile
+     * (a pair) each leave their unnormalised partial result in the
+     * workspace, and the one that finishes second merges both.  16-byte
+     * aligned device array. */
+    const int32_t *prefill_units;     /* [num_prefill_units][4]: tile, step_lo, step_hi,
+                                         2 * pair + (0 lower keys, 1 upper keys), or -1 */
+    int32_t num_prefill_units;        /* host: 0 = one unit per tile, in tile order */
+    int32_t num_prefill_pairs;        /* host: split tiles in the plan */
+    void *prefill_workspace;          /* device, zeroed before its first use */
+    size_t prefill_workspace_bytes;   /* host: its size, >= astr_prefill_workspace_bytes(
+                                         num_prefill_pairs, n_heads, head_dim) */
 } astr_kv_meta;
 
 /* Message for the last non-OK status returned on the calling thread. */
@@ -266,11 +282,66 @@ int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, 
  *   m     host; uses the pool fields, req_to_token, num_reqs, max_ctx_len,
  *         req_pool_indices, kv_indptr, qo_indptr, q_tile_to_batch,
  *         q_tile_to_index, batch, max_len, num_q_tiles, q_tile
- *         (q_tile must be 64)
- * sm_scale <= 0 means 1/sqrt(head_dim).  Errors: INVAL, UNSUPPORTED, LAUNCH.
+ *         (q_tile must be 64), and the optional work plan (prefill_units,
+ *         num_prefill_units, num_prefill_pairs, prefill_workspace)
+ * sm_scale <= 0 means 1/sqrt(head_dim).  A plan changes the order of the
+ * softmax sums, not the result beyond rounding.  Errors: INVAL (also: a plan
+ * without workspace, a workspace smaller than its plan needs, units not
+ * 16-byte aligned, more units than 16 * num_q_tiles), UNSUPPORTED, LAUNCH.
  */
 int astr_prefill_attn(const void *q, void *out, int total_q, int n_heads,
                       const astr_kv_meta *m, int layer_id, float sm_scale, void *stream);
+
+/*
+ * Workspace of a prefill work plan with `pairs` split tiles: per pair, KV
+ * head and group of 4 query heads, a completion count (int32) and the two
+ * units' partial results (the float32 O accumulators and, per row, the
+ * running max and the row sum).  The counts must be zero before the first
+ * call that uses the workspace; every call leaves them zero again.  Calls
+ * that share a workspace must not run concurrently.  The layout is that of
+ * the head_dim-128 kernel, the only one that follows plans.  0 for no pairs
+ * and on bad input.
+ */
+size_t astr_prefill_workspace_bytes(int pairs, int n_heads, int head_dim);
+
+/*
+ * The prefill work plan of a step (host only).  Its reading of the pages:
+ * the pages tile prefill work by query tiles (inference.md, "KVCache
+ * System") and leave open how tiles are scheduled.  With one workgroup per
+ * compute unit, a batch whose longest tiles carry much more than the mean
+ * load finishes when its longest tile does; splitting such a tile's keys in
+ * two halves shortens that critical path.  The halves merge as the decode
+ * splits do (inference.md, "KVCache System": split-K partial outputs kept
+ * with their partial max and sum, from which the softmax over the union of
+ * the key sets follows exactly).
+ * Rule: tile t sees n_t = ceil(kv_end_t / 32) key steps, kv_end_t = p_b +
+ * row0 + rows (0 steps for a tile with inconsistent metadata).  Costs, in
+ * steps of 32 keys (measured on MI355X: ~1 us per step, ~5 us of prologue,
+ * ~2 us to store a tile's output, ~3 us to publish a half's state, ~3 us to
+ * merge): a whole tile 7 + n_t (0.1 when skipped), a lower half [0, h) 8.5
+ * + h, an upper half [h, end) 9.5 + n_t - h, h = n_t / 2.  For each split
+ * set {t : n_t >= 2, n_t > T}, T = floor(max_t n_t * k / 10), k = 9 .. 3,
+ * and for no split, the units are listed by decreasing cost (ties: tile
+ * order, then lower half first) and dealt to the 8 XCDs in that order, each
+ * to the XCD where it would end first (ties: fewer units queued, then the
+ * lower XCD); an XCD runs its queue in order on num_cus / 8 compute units,
+ * one workgroup per compute unit, the unit's workgroups_per_tile workgroups
+ * on the ones free first.  The split set with the earliest simulated end
+ * wins if it ends at least 10% before the unsplit list.  Entry 8k + x of the
+ * plan is the k-th unit of XCD x (the kernel runs unit u on XCD u % 8);
+ * shorter queues are padded with units of tile -1, which do nothing.
+ *   qo_indptr, kv_indptr  host [batch + 1]; q_tile_to_batch, q_tile_to_index
+ *   host [num_q_tiles]; q_tile rows per tile (64); workgroups_per_tile
+ *   = n_heads / 4 for the kernel that follows plans; num_cus >= 8
+ *   units       host [capacity][4], written (layout of astr_kv_meta.prefill_units)
+ *   *num_units, *num_pairs  written
+ * capacity >= 16 * num_q_tiles always suffices.
+ * Errors: INVAL (null pointer, negative size, num_cus < 8, capacity short).
+ */
+int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_indptr, int batch,
+                      const int32_t *q_tile_to_batch, const int32_t *q_tile_to_index, int num_q_tiles,
+                      int q_tile, int workgroups_per_tile, int num_cus, int32_t *units, int capacity,
+                      int *num_units, int *num_pairs);
 
 /* ------------------------------------------------------------------------ */
 /* Page-table builder (host only; no device calls)                          */

@@ -18,7 +18,8 @@ ASTR_BF16 = 1
 EXPORTS = (
     "astr_last_error", "astr_rope_table", "astr_rope_kv_write", "astr_rope_backward",
     "astr_decode_num_splits", "astr_decode_split_items", "astr_decode_attn_write",
-    "astr_decode_attn", "astr_prefill_attn", "astr_pagepool_create", "astr_pagepool_destroy",
+    "astr_decode_attn", "astr_prefill_attn", "astr_prefill_workspace_bytes", "astr_prefill_plan",
+    "astr_pagepool_create", "astr_pagepool_destroy",
     "astr_pagepool_admit", "astr_pagepool_extend", "astr_pagepool_bind", "astr_pagepool_insert",
     "astr_pagepool_release", "astr_pagepool_table", "astr_pagepool_free_pages",
     "astr_pagepool_page_ref", "astr_pagepool_complete", "astr_pagepool_evict",
@@ -41,6 +42,9 @@ class KvMeta(ctypes.Structure):
         ("num_q_tiles", ctypes.c_int32), ("q_tile", ctypes.c_int32),
         ("split_item_batch", c_vp), ("split_item_index", c_vp),
         ("num_split_items", ctypes.c_int32), ("split_item_chunk", ctypes.c_int32),
+        ("prefill_units", c_vp), ("num_prefill_units", ctypes.c_int32),
+        ("num_prefill_pairs", ctypes.c_int32), ("prefill_workspace", c_vp),
+        ("prefill_workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -69,6 +73,10 @@ def lib():
                                          c_int, c_int, ctypes.c_float, c_vp, c_vp, c_vp]
     L.astr_prefill_attn.argtypes = [c_vp, c_vp, c_int, c_int, ctypes.POINTER(KvMeta), c_int,
                                     ctypes.c_float, c_vp]
+    L.astr_prefill_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.astr_prefill_workspace_bytes.restype = ctypes.c_size_t
+    L.astr_prefill_plan.argtypes = [c_i32p, c_i32p, c_int, c_i32p, c_i32p, c_int, c_int, c_int, c_int,
+                                    c_i32p, c_int, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
     L.astr_pagepool_create.argtypes = [ctypes.POINTER(c_vp), c_int, ctypes.c_int64, c_int, c_int,
                                        c_int, c_i32p]
     L.astr_pagepool_destroy.argtypes = [c_vp]

@@ -76,6 +76,10 @@ class KVCache:
     split_item_index: Optional[torch.Tensor] = None
     num_split_items: int = 0
     split_item_chunk: int = 0
+    # prefill work plan ([n, 4] int32 units) and its workspace; optional
+    prefill_units: Optional[torch.Tensor] = None
+    num_prefill_pairs: int = 0
+    prefill_workspace: Optional[torch.Tensor] = None
 
     @property
     def batch(self) -> int:
@@ -96,10 +100,36 @@ def decode_split_items(seq_lens, split_chunk: int):
     return ib[:n.value], ix[:n.value]
 
 
+def prefill_plan(meta: dict, n_heads: int, num_cus: int = 256):
+    """Host prefill work plan of a bound step (astr_prefill_plan) for a model
+    with n_heads query heads; returns ([n, 4] int32 units, number of pairs)."""
+    _need(n_heads >= 4, "the prefill plan is for 4 or more query heads")
+    nt = int(meta["num_q_tiles"])
+    qo, kv = _i32(meta["qo_indptr"]), _i32(meta["kv_indptr"])
+    t2b, t2i = _i32(meta["q_tile_to_batch"])[:nt], _i32(meta["q_tile_to_index"])[:nt]
+    cap = max(16 * nt, 8)
+    units = np.zeros((cap, 4), np.int32)
+    n, pairs = ctypes.c_int(), ctypes.c_int()
+    check(lib().astr_prefill_plan(_i32p(qo), _i32p(kv), int(qo.size) - 1, _i32p(t2b), _i32p(t2i), nt,
+                                  int(meta["q_tile"]), int(n_heads) // 4, int(num_cus), _i32p(units), cap,
+                                  ctypes.byref(n), ctypes.byref(pairs)))
+    return units[:n.value].copy(), pairs.value
+
+
+def prefill_workspace_bytes(pairs: int, n_heads: int, head_dim: int) -> int:
+    return int(lib().astr_prefill_workspace_bytes(int(pairs), int(n_heads), int(head_dim)))
+
+
 def cache_from_bind(k_buffer: torch.Tensor, v_buffer: torch.Tensor, table: np.ndarray,
-                    meta: dict, split_chunk: Optional[int] = None) -> KVCache:
+                    meta: dict, split_chunk: Optional[int] = None, prefill_heads: Optional[int] = None,
+                    prefill_workspace: Optional[torch.Tensor] = None, num_cus: int = 256) -> KVCache:
     """Upload one step's host metadata (PagePool.bind) next to the pool; with
-    split_chunk, also the decode work items for that chunk."""
+    split_chunk, also the decode work items for that chunk; with prefill_heads
+    (the query heads of the prefill call), also the prefill work plan and a
+    workspace for it (prefill_workspace is used when large enough, else a
+    zeroed one is allocated).  Only the bf16 head_dim-128 prefill with a
+    multiple of 4 query heads per KV head follows plans; for other pools no
+    plan is built."""
     dev = k_buffer.device
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
     c = KVCache(k_buffer=k_buffer, v_buffer=v_buffer, req_to_token=up(table),
@@ -113,6 +143,18 @@ def cache_from_bind(k_buffer: torch.Tensor, v_buffer: torch.Tensor, table: np.nd
         ib, ix = decode_split_items(meta["seq_lens"], split_chunk)
         c.split_item_batch, c.split_item_index = up(ib), up(ix)
         c.num_split_items, c.split_item_chunk = int(ib.size), int(split_chunk)
+    n_kv, hd = int(k_buffer.shape[2]), int(k_buffer.shape[3])
+    if (prefill_heads is not None and int(meta["num_q_tiles"]) > 0 and k_buffer.dtype == torch.bfloat16
+            and hd == 128 and prefill_heads % n_kv == 0 and (prefill_heads // n_kv) % 4 == 0):
+        units, pairs = prefill_plan(meta, prefill_heads, num_cus)
+        c.prefill_units = up(units)
+        c.num_prefill_pairs = pairs
+        need = prefill_workspace_bytes(pairs, prefill_heads, hd)
+        if need > 0:
+            if prefill_workspace is not None and prefill_workspace.numel() * prefill_workspace.element_size() >= need:
+                c.prefill_workspace = prefill_workspace
+            else:
+                c.prefill_workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     return c
 
 
@@ -142,6 +184,15 @@ def _meta(c: KVCache, need_prefill: bool = False) -> KvMeta:
         m.split_item_batch = c.split_item_batch.data_ptr()
         m.split_item_index = c.split_item_index.data_ptr()
         m.num_split_items, m.split_item_chunk = int(c.num_split_items), int(c.split_item_chunk)
+    if need_prefill and c.prefill_units is not None:
+        _dev_tensor(c.prefill_units, "prefill_units", torch.int32, kb.device)
+        _need(c.prefill_units.dim() == 2 and c.prefill_units.shape[1] == 4, "prefill_units must be [n, 4]")
+        m.prefill_units = c.prefill_units.data_ptr()
+        m.num_prefill_units, m.num_prefill_pairs = int(c.prefill_units.shape[0]), int(c.num_prefill_pairs)
+        if c.prefill_workspace is not None:
+            _dev_tensor(c.prefill_workspace, "prefill_workspace", device=kb.device)
+            m.prefill_workspace = c.prefill_workspace.data_ptr()
+            m.prefill_workspace_bytes = c.prefill_workspace.numel() * c.prefill_workspace.element_size()
     if need_prefill:
         _dev_tensor(c.qo_indptr, "qo_indptr", torch.int32, kb.device, b + 1)
         _dev_tensor(c.q_tile_to_batch, "q_tile_to_batch", torch.int32, kb.device, c.num_q_tiles)

@@ -263,5 +263,41 @@ extern "C" int astr_prefill_attn(const void *q, void *out, int total_q, int n_he
     a.q_tile = m->q_tile;
     a.n_heads = n_heads;
     a.scale_log2 = astr::scale_of(sm_scale, m->head_dim);
+    if (m->prefill_units || m->num_prefill_units || m->num_prefill_pairs) {
+        if (!m->prefill_units || m->num_prefill_units < 1 || m->num_prefill_pairs < 0)
+            return fail(ASTR_E_INVAL, "prefill_attn: incomplete work plan");
+        if (reinterpret_cast<uintptr_t>(m->prefill_units) % 16 != 0)
+            return fail(ASTR_E_INVAL, "prefill_attn: work plan units not 16-byte aligned");
+        if (m->num_prefill_pairs > 0 && !m->prefill_workspace)
+            return fail(ASTR_E_INVAL, "prefill_attn: a plan with %d split tiles needs a workspace",
+                        m->num_prefill_pairs);
+        if (m->num_prefill_units > 16 * static_cast<int64_t>(m->num_q_tiles) ||
+            static_cast<int64_t>(m->num_prefill_units) * m->n_kv_heads * ((n_heads / m->n_kv_heads + 3) / 4) +
+                    8 * 64 > INT32_MAX ||
+            astr::prefill_part_slots(m->num_prefill_pairs, n_heads) * 2 * astr::kPrefillPartFloats >
+                INT64_MAX / 8)
+            return fail(ASTR_E_INVAL, "prefill_attn: work plan too large for %d tiles", m->num_q_tiles);
+        if (m->num_prefill_pairs > 0 &&
+            m->prefill_workspace_bytes < astr_prefill_workspace_bytes(m->num_prefill_pairs, n_heads, m->head_dim))
+            return fail(ASTR_E_INVAL, "prefill_attn: workspace of %zu bytes, the plan needs %zu",
+                        m->prefill_workspace_bytes,
+                        astr_prefill_workspace_bytes(m->num_prefill_pairs, n_heads, m->head_dim));
+        a.units = m->prefill_units;
+        a.num_units = m->num_prefill_units;
+        a.num_pairs = m->num_prefill_pairs;
+        const int64_t slots = astr::prefill_part_slots(m->num_prefill_pairs, n_heads);
+        a.part_cnt = static_cast<int32_t *>(m->prefill_workspace);
+        a.part = m->num_prefill_pairs > 0
+                     ? reinterpret_cast<float *>(static_cast<char *>(m->prefill_workspace) +
+                                                 astr::prefill_counts_bytes(slots))
+                     : nullptr;
+    }
     return astr::launched("prefill_attn", astr::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" size_t astr_prefill_workspace_bytes(int pairs, int n_heads, int head_dim) {
+    if (pairs < 0 || n_heads < 1 || head_dim < 1) return 0;
+    if (pairs == 0) return 0;
+    const int64_t slots = astr::prefill_part_slots(pairs, n_heads);
+    return static_cast<size_t>(astr::prefill_counts_bytes(slots) + slots * 2 * astr::kPrefillPartFloats * 4);
 }

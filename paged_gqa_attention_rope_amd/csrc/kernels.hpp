@@ -74,7 +74,22 @@ struct PrefillArgs {
     int q_tile;
     int n_heads;
     float scale_log2;
+    // work plan (num_units 0: one unit per tile); part_cnt / part: workspace
+    const int32_t *units;
+    int num_units;
+    int num_pairs;
+    int32_t *part_cnt;
+    float *part;
 };
+
+// Prefill workspace of a plan: per (pair, KV head, group of 4 query heads) a
+// completion count, then two partial results of kPrefillPartFloats floats:
+// O^T accumulators [8 waves][2 heads][8 column blocks][4][64 lanes] and
+// (max, sum) [8 waves][2 heads][2][64 lanes] (lanes innermost, so that one
+// store or load of a wave covers 256 contiguous bytes).
+constexpr int64_t kPrefillPartFloats = 8 * 2 * 8 * 64 * 4 + 8 * 2 * 64 * 2;
+inline int64_t prefill_part_slots(int64_t pairs, int n_heads) { return pairs * ((n_heads + 3) / 4); }
+inline int64_t prefill_counts_bytes(int64_t slots) { return (4 * slots + 255) / 256 * 256; }
 
 // Largest byte stride of a structured-buffer record (14-bit field); the bf16
 // prefill addresses the pool as records of this size or less.

@@ -549,3 +549,158 @@ extern "C" int astr_decode_split_items(const int32_t *seq_lens, int batch, int s
     *num_items = n;
     return ASTR_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Prefill work plan: which query tiles to split by keys, and on which XCD and
+// in which order the units run.  The cost model and the rule are the ones
+// documented with astr_prefill_plan.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kPlanXcds = 8;               // the prefill kernel deals units to 8 XCDs
+constexpr int kPlanStep = 32;              // keys per step of the kernel
+constexpr double kWhole = 7.0;             // per whole tile: prologue and output, in steps
+constexpr double kLower = 8.5;             // lower half: prologue and publishing its state
+constexpr double kUpper = 9.5;             // upper half: prologue, merge and output
+constexpr double kEmpty = 0.1;             // a tile the kernel skips
+
+struct PlanUnit {
+    double cost;
+    int tile, piece;                       // piece -1: whole tile (or padding when tile is -1)
+    int lo, hi;                            // key steps [lo, hi)
+};
+
+// Units of the tiles, those with more than `thr` steps split in two halves,
+// by decreasing cost (ties: tile order, then lower half first).
+std::vector<PlanUnit> plan_units(const std::vector<int> &steps, int thr) {
+    std::vector<PlanUnit> list;
+    list.reserve(2 * steps.size());
+    for (int t = 0; t < static_cast<int>(steps.size()); ++t) {
+        const int n = steps[t];
+        if (n >= 2 && n > thr) {
+            const int h = n / 2;
+            list.push_back({kLower + h, t, 0, 0, h});
+            list.push_back({kUpper + (n - h), t, 1, h, INT32_MAX});
+        } else {
+            list.push_back({n > 0 ? kWhole + n : kEmpty, t, -1, 0, INT32_MAX});
+        }
+    }
+    std::stable_sort(list.begin(), list.end(), [](const PlanUnit &a, const PlanUnit &b) {
+        if (a.cost != b.cost) return a.cost > b.cost;
+        if (a.tile != b.tile) return a.tile < b.tile;
+        return a.piece < b.piece;
+    });
+    return list;
+}
+
+// Deal a cost-ordered list to the XCDs: each unit goes to the XCD where it
+// would end first (ties: fewer units queued, then the lower XCD); an XCD
+// runs its queue in order on cus_per_xcd compute units, one workgroup per
+// compute unit, the unit's wg_per_unit workgroups on the ones free first.
+// Returns the simulated end; queue[x] receives the units of XCD x.
+double deal(const std::vector<PlanUnit> &list, int wg_per_unit, int cus_per_xcd,
+            std::vector<std::vector<int>> &queue) {
+    std::vector<std::multiset<double>> free_at(kPlanXcds);
+    for (auto &f : free_at)
+        for (int c = 0; c < cus_per_xcd; ++c) f.insert(0.0);
+    queue.assign(kPlanXcds, {});
+    const int wg = std::min(wg_per_unit, cus_per_xcd);
+    double end = 0.0;
+    for (int i = 0; i < static_cast<int>(list.size()); ++i) {
+        int best = 0;
+        double best_end = 0.0;
+        for (int x = 0; x < kPlanXcds; ++x) {
+            // the unit's last workgroup starts when its wg-th compute unit frees
+            auto it = free_at[x].begin();
+            std::advance(it, wg - 1);
+            const double e = *it + list[i].cost;
+            if (x == 0 || e < best_end || (e == best_end && queue[x].size() < queue[best].size())) {
+                best = x;
+                best_end = e;
+            }
+        }
+        for (int w = 0; w < wg_per_unit; ++w) {
+            const double t = *free_at[best].begin() + list[i].cost;
+            free_at[best].erase(free_at[best].begin());
+            free_at[best].insert(t);
+            end = std::max(end, t);
+        }
+        queue[best].push_back(i);
+    }
+    return end;
+}
+
+}  // namespace
+
+extern "C" int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_indptr, int batch,
+                                 const int32_t *q_tile_to_batch, const int32_t *q_tile_to_index,
+                                 int num_q_tiles, int q_tile, int workgroups_per_tile, int num_cus,
+                                 int32_t *units, int capacity, int *num_units, int *num_pairs) {
+    if (!qo_indptr || !kv_indptr || !num_units || !num_pairs || batch < 0 || num_q_tiles < 0 ||
+        q_tile < 1 || workgroups_per_tile < 1 || num_cus < kPlanXcds || capacity < 0 ||
+        (num_q_tiles > 0 && (!q_tile_to_batch || !q_tile_to_index || !units)))
+        return astr::fail(ASTR_E_INVAL, "prefill_plan: bad argument");
+    // key steps seen by each tile (0 for a tile the kernel skips)
+    std::vector<int> steps(num_q_tiles, 0);
+    int max_steps = 0;
+    for (int t = 0; t < num_q_tiles; ++t) {
+        const int b = q_tile_to_batch[t];
+        const int64_t idx = q_tile_to_index[t];
+        if (b < 0 || b >= batch || idx < 0) continue;
+        const int64_t e = static_cast<int64_t>(qo_indptr[b + 1]) - qo_indptr[b];
+        const int64_t p = static_cast<int64_t>(kv_indptr[b + 1]) - kv_indptr[b] - e;
+        const int64_t row0 = idx * q_tile;
+        if (e <= 0 || p < 0 || row0 >= e) continue;
+        const int64_t kv_end = p + row0 + std::min<int64_t>(q_tile, e - row0);
+        steps[t] = static_cast<int>(std::min<int64_t>((kv_end + kPlanStep - 1) / kPlanStep, INT32_MAX / 2));
+        max_steps = std::max(max_steps, steps[t]);
+    }
+    const int cus_per_xcd = num_cus / kPlanXcds;
+    std::vector<std::vector<int>> queue, cand_queue;
+    std::vector<PlanUnit> best = plan_units(steps, INT32_MAX);
+    const double base_end = deal(best, workgroups_per_tile, cus_per_xcd, queue);
+    double best_end = base_end;
+    std::vector<PlanUnit> chosen;
+    std::vector<std::vector<int>> chosen_queue;
+    for (int k = 9; k >= 3; --k) {
+        const int thr = static_cast<int>(static_cast<int64_t>(max_steps) * k / 10);
+        std::vector<PlanUnit> cand = plan_units(steps, thr);
+        const double end = deal(cand, workgroups_per_tile, cus_per_xcd, cand_queue);
+        if (end < best_end) {
+            best_end = end;
+            chosen.swap(cand);
+            chosen_queue.swap(cand_queue);
+        }
+    }
+    if (!chosen.empty() && best_end <= 0.90 * base_end) {
+        best.swap(chosen);
+        queue.swap(chosen_queue);
+    }
+    // position 8k + x holds the k-th unit of XCD x; shorter queues are padded
+    size_t len = 0;
+    for (const auto &q : queue) len = std::max(len, q.size());
+    const int64_t n = static_cast<int64_t>(len) * kPlanXcds;
+    if (n > capacity)
+        return astr::fail(ASTR_E_INVAL, "prefill_plan: %lld units, capacity %d", static_cast<long long>(n), capacity);
+    std::vector<int> pair_of(num_q_tiles, -1);
+    int pairs = 0;
+    for (size_t k = 0; k < len; ++k) {
+        for (int x = 0; x < kPlanXcds; ++x) {
+            int32_t *row = units + 4 * (kPlanXcds * k + x);
+            if (k >= queue[x].size()) {
+                row[0] = -1, row[1] = 0, row[2] = 0, row[3] = -1;
+                continue;
+            }
+            const PlanUnit &u = best[queue[x][k]];
+            int pw = -1;
+            if (u.piece >= 0) {
+                if (pair_of[u.tile] < 0) pair_of[u.tile] = pairs++;
+                pw = 2 * pair_of[u.tile] + u.piece;
+            }
+            row[0] = u.tile, row[1] = u.lo, row[2] = u.hi, row[3] = pw;
+        }
+    }
+    *num_units = static_cast<int>(n);
+    *num_pairs = pairs;
+    return ASTR_OK;
+}

@@ -791,7 +791,8 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     const int32_t *__restrict__ req_pool_indices, const int32_t *__restrict__ qo_indptr,
     const int32_t *__restrict__ kv_indptr, const int32_t *__restrict__ q_tile_to_batch,
     const int32_t *__restrict__ q_tile_to_index, int batch, int total_q, int n_heads,
-    int num_q_tiles, float scale_log2) {
+    int num_q_tiles, float scale_log2, const int32_t *__restrict__ units, int num_units, int num_pairs,
+    int32_t *__restrict__ part_cnt, float *__restrict__ part) {
     using C = PpCfg;
     constexpr int D = C::D, TQ = C::TQ, HW = C::HW, KS = C::KS, DB = C::DB, SL = C::SL, RB = C::RB;
     constexpr int MAT = C::MAT, SLOT = C::SLOT, TS = C::TS, NB = C::NB, NI = C::NI, RPI = C::RPI;
@@ -800,14 +801,25 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     constexpr float kLazy = 8.f;
     static_assert(G % 4 == 0, "4 query heads per workgroup");
 
-    // tiles dealt to the 8 XCDs heaviest first, as in prefill_mfma_kernel
+    // units (tiles, or the key halves of a plan's split tiles) dealt to the
+    // 8 XCDs in list order, heaviest first, as in prefill_mfma_kernel
     const int units_per_tile = n_kv * GROUPS;
     const int xcd = blockIdx.x % kXcds, k_in = blockIdx.x / kXcds;
-    const int tile = kXcds * (k_in / units_per_tile) + xcd;
-    if (tile >= num_q_tiles) return;
+    const int unit = kXcds * (k_in / units_per_tile) + xcd;
     const int u = k_in % units_per_tile;
     const int kvh = u / GROUPS;
     const int hg = u % GROUPS;
+    int tile = unit, step_lo = 0, step_hi = INT_MAX, pw = -1;
+    if (num_units > 0) {
+        if (unit >= num_units) return;
+        const int4 d = reinterpret_cast<const int4 *>(units)[unit];
+        tile = d.x;
+        step_lo = d.y;
+        step_hi = d.z;
+        pw = d.w < 0 ? -1 : d.w;
+        if (step_lo < 0 || pw >= 2 * num_pairs) return;     // not a plan's unit
+    }
+    if (tile < 0 || tile >= num_q_tiles) return;
     TileInfo ti;
     if (!tile_info(tile, q_tile_to_batch, q_tile_to_index, qo_indptr, kv_indptr,
                    req_pool_indices, batch, num_reqs, max_ctx_len, total_q, TQ, ti))
@@ -821,7 +833,10 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     const int h0 = kvh * G + 4 * hg + 2 * (wave >> 2); // first query head of this wave
     const int qpos0 = ti.p + ti.row0 + r0;
     const int qpos = qpos0 + j;
-    const int nsteps = (ti.kv_end + TS - 1) / TS;
+    // this unit's key steps [t0, t1), and the keys its copies may fetch
+    const int t0 = step_lo;
+    const int t1 = min(step_hi, (ti.kv_end + TS - 1) / TS);
+    const int kv_lim = min(ti.kv_end, TS * t1);
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NB * SLOT];
     auto slot_ptr = [&](auto rc) -> uint8_t * {
@@ -906,7 +921,7 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     };
     // this lane's row's slot index of step t (its index copy has landed)
     auto slot_index = [&](int t) -> int32_t { return sidx[t & (NI - 1)][wave][lane / SL]; };
-    // rows of step t into ring slot R (t >= nsteps, or past the visible keys:
+    // rows of step t into ring slot R (t >= t1, or past the visible keys:
     // out-of-range records, which read zeros; the copy count never changes)
     auto issue = [&](auto rc, int t, int32_t sl) {
         constexpr int R = decltype(rc)::value;
@@ -914,7 +929,7 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         uint32_t rec;
         if constexpr (WIDE) rec = ok ? static_cast<uint32_t>(sl) * n_kv + kvh : 0xffffffffu;
         else rec = static_cast<uint32_t>(sl);
-        if (crow >= ti.kv_end - TS * t) rec = 0xffffffffu;
+        if (crow >= kv_lim - TS * t) rec = 0xffffffffu;
         const uint32_t dk = lds_addr(slot_ptr(rc)) + RB * RPI * wave;
         copy_record16_to_lds(krs, rec, ccol, dk);
         copy_record16_to_lds(vrs, rec, ccol, dk + MAT);
@@ -1053,96 +1068,166 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     // for them at the end of its VALU(t-2), when 6 copies have been issued
     // after them (for group A one phase earlier than needed, which costs
     // nothing measurable and keeps every wait a constant count).
-    // prologue: indices of steps 0..5, rows of steps 0..3, in the order
-    // that puts exactly 6 copies after the rows of step 2 by the end of
-    // VALU(0), as in every later step (each index copy waited for by the
-    // count of copies issued after it)
-    for (int t = 0; t < 5; ++t) fetch_idx(t);
-    wait_copies<4>();
-    issue(int_c<0>{}, 0, slot_index(0));
-    wait_copies<5>();
-    issue(int_c<1>{}, 1, slot_index(1));
-    wait_copies<6>();
-    issue(int_c<2>{}, 2, slot_index(2));
-    fetch_idx(5);
-    wait_copies<8>();
-    issue(int_c<3>{}, 3, slot_index(3));
-    wait_copies<7>();                                  // rows of step 0
-    phase_end();
-    if (grp_b) {                                       // B: idle first phase
-        wait_copies<5>();                              // rows of step 1
-        phase_end();
-    }
-    f32x4_t sc[HW][2];
-    {
-        Frag8 kf[KS][2];
-        load_k(int_c<0>{}, kf);
-        __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0)
-        qk(kf, sc);
-        pin(sc);
-    }
-    if (!grp_b) wait_copies<5>();                      // A: rows of step 1
-    phase_end();
-
-    // keys of step 0 with a slot in the pool (its indices landed in the prologue)
-    uint32_t okw_cur = ok_bits(idx_of_step(0));
-    // first step whose keys cross the causal diagonal of this wave's first row
-    const int s_diag = (qpos0 + 1) / TS;
-    // one step: VALU(s), then MFMA(s); true after the last one
-    auto step = [&](auto rc, int s) -> bool {
-        constexpr int R = decltype(rc)::value;
-        constexpr int R1 = (R + 1) % NB, R4 = (R + 4) % NB;
-        const bool more = s + 1 < nsteps;
-        // the small LDS reads first (LDS reads complete in order, so nothing
-        // below waits for the K operands): the slot indices of step s+4, whose
-        // copy has landed (5 copies were issued after it), and the 32 slot
-        // indices of step s+1; then the K operands of step s+1
+    // Steps are numbered from the unit's first, t0 (0 for a whole tile); the
+    // ring slot of step t is (t - t0) % NB.  A unit with no steps (a plan's
+    // upper half past a short tile's end) keeps the empty state.
+    if (t0 < t1) {
+        // prologue: indices of steps t0..t0+5, rows of steps t0..t0+3, in the
+        // order that puts exactly 6 copies after the rows of step t0+2 by the
+        // end of VALU(t0), as in every later step (each index copy waited for
+        // by the count of copies issued after it)
+        for (int t = t0; t < t0 + 5; ++t) fetch_idx(t);
+        wait_copies<4>();
+        issue(int_c<0>{}, t0, slot_index(t0));
         wait_copies<5>();
-        const int32_t sl4 = slot_index(s + 4);
-        // step s+1's keys with a slot in the pool, as a scalar mask for
-        // VALU(s+1), so that no phase waits for the read
-        const int32_t nix = idx_of_step(s + 1);
-        const uint32_t okw = okw_cur;
-        // (K is read unconditionally, so that the compiler's count of
-        // outstanding LDS reads stays exact; after the last step it goes unused)
-        Frag8 kf[KS][2], vf[DB], pf[HW];
-        load_k(int_c<R1>{}, kf);
-        {
-            float lm[HW], alpha[HW];
-            if (__builtin_expect(s >= s_diag || okw != 0xffffffffu, 0)) apply_mask(sc, TS * s, okw);
-            local_max(sc, lm);
-            if (__builtin_expect(update_max(lm, alpha, sc), 0)) rescale(alpha);
-        }
-        probs(sc, pf);
-        pin(pf);                                       // P(s) is formed in this phase
-        fetch_idx(s + 6);
-        issue(int_c<R4>{}, s + 4, sl4);
-        okw_cur = ok_bits(nix);
-        // rows of step s+2 (6 copies were issued after them): group B reads
-        // K(s+2) in its next phase; group A only after its MFMA(s)
+        issue(int_c<1>{}, t0 + 1, slot_index(t0 + 1));
         wait_copies<6>();
+        issue(int_c<2>{}, t0 + 2, slot_index(t0 + 2));
+        fetch_idx(t0 + 5);
+        wait_copies<8>();
+        issue(int_c<3>{}, t0 + 3, slot_index(t0 + 3));
+        wait_copies<7>();                              // rows of step t0
         phase_end();
-        load_v(rc, vf);
-        if (more) {
-            qk(kf, sc);
-            pin(sc);                                   // S(s+1) is formed in this phase
+        if (grp_b) {                                   // B: idle first phase
+            wait_copies<5>();                          // rows of step t0+1
+            phase_end();
         }
-        pv(vf, pf);
-        pin(o);
-        pin(osum);
+        f32x4_t sc[HW][2];
+        {
+            Frag8 kf[KS][2];
+            load_k(int_c<0>{}, kf);
+            __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0)
+            qk(kf, sc);
+            pin(sc);
+        }
+        if (!grp_b) wait_copies<5>();                  // A: rows of step t0+1
         phase_end();
-        return !more;
-    };
-    for (int s = 0;; s += NB) {
-        if (step(int_c<0>{}, s)) break;
-        if (step(int_c<1>{}, s + 1)) break;
-        if (step(int_c<2>{}, s + 2)) break;
-        if (step(int_c<3>{}, s + 3)) break;
-        if (step(int_c<4>{}, s + 4)) break;
-        if (step(int_c<5>{}, s + 5)) break;
+
+        // keys of step t0 with a slot in the pool (its indices landed in the prologue)
+        uint32_t okw_cur = ok_bits(idx_of_step(t0));
+        // first step whose keys cross the causal diagonal of this wave's first row
+        const int s_diag = (qpos0 + 1) / TS;
+        // one step: VALU(s), then MFMA(s); true after the last one
+        auto step = [&](auto rc, int s) -> bool {
+            constexpr int R = decltype(rc)::value;
+            constexpr int R1 = (R + 1) % NB, R4 = (R + 4) % NB;
+            const bool more = s + 1 < t1;
+            // the small LDS reads first (LDS reads complete in order, so nothing
+            // below waits for the K operands): the slot indices of step s+4, whose
+            // copy has landed (5 copies were issued after it), and the 32 slot
+            // indices of step s+1; then the K operands of step s+1
+            wait_copies<5>();
+            const int32_t sl4 = slot_index(s + 4);
+            // step s+1's keys with a slot in the pool, as a scalar mask for
+            // VALU(s+1), so that no phase waits for the read
+            const int32_t nix = idx_of_step(s + 1);
+            const uint32_t okw = okw_cur;
+            // (K is read unconditionally, so that the compiler's count of
+            // outstanding LDS reads stays exact; after the last step it goes unused)
+            Frag8 kf[KS][2], vf[DB], pf[HW];
+            load_k(int_c<R1>{}, kf);
+            {
+                float lm[HW], alpha[HW];
+                if (__builtin_expect(s >= s_diag || okw != 0xffffffffu, 0)) apply_mask(sc, TS * s, okw);
+                local_max(sc, lm);
+                if (__builtin_expect(update_max(lm, alpha, sc), 0)) rescale(alpha);
+            }
+            probs(sc, pf);
+            pin(pf);                                   // P(s) is formed in this phase
+            fetch_idx(s + 6);
+            issue(int_c<R4>{}, s + 4, sl4);
+            okw_cur = ok_bits(nix);
+            // rows of step s+2 (6 copies were issued after them): group B reads
+            // K(s+2) in its next phase; group A only after its MFMA(s)
+            wait_copies<6>();
+            phase_end();
+            load_v(rc, vf);
+            if (more) {
+                qk(kf, sc);
+                pin(sc);                               // S(s+1) is formed in this phase
+            }
+            pv(vf, pf);
+            pin(o);
+            pin(osum);
+            phase_end();
+            return !more;
+        };
+        for (int s = t0;; s += NB) {
+            if (step(int_c<0>{}, s)) break;
+            if (step(int_c<1>{}, s + 1)) break;
+            if (step(int_c<2>{}, s + 2)) break;
+            if (step(int_c<3>{}, s + 3)) break;
+            if (step(int_c<4>{}, s + 4)) break;
+            if (step(int_c<5>{}, s + 5)) break;
+        }
+        if (!grp_b) phase_end();                       // A: idle last phase
+        wait_copies<0>();
     }
-    if (!grp_b) phase_end();                           // A: idle last phase
-    wait_copies<0>();
+
+    if (pw >= 0) {
+        // One half of a split tile.  Each half leaves its unnormalised state
+        // (O^T accumulators, running max m and row sum l of every row) in its
+        // part of the workspace and counts itself done; the half that counts
+        // second merges the other's state into its own and writes the output
+        // (a row's softmax over both key sets: M = max(m, m'), weights
+        // 2^(m - M) and 2^(m' - M) on the sums and accumulators).  The state
+        // is written with agent-coherent stores, all complete before the
+        // count (vector memory counter at zero), and read back with
+        // agent-coherent loads issued after the count was seen, so the halves
+        // may run on any two XCDs; no wave ever waits for another workgroup.
+        constexpr int64_t kPart = kPrefillPartFloats;
+        constexpr int kML = WAVES * HW * DB * 64 * 4;    // offset of (m, l) in a part
+        static_assert(kML + WAVES * HW * 64 * 2 == kPart, "workspace layout");
+        const int64_t ps = (static_cast<int64_t>(pw >> 1) * n_kv + kvh) * GROUPS + hg;
+        int32_t *cnt = part_cnt + ps;
+        float *mine = part + (2 * ps + (pw & 1)) * kPart;
+        const float *other = part + (2 * ps + ((pw & 1) ^ 1)) * kPart;
+        __shared__ int32_t seen;
+        // has the other half already published its state?
+        if (tid == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (seen == 0) {
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __hip_atomic_store(mine + (((wave * HW + hh) * DB + db) * 4 + e) * 64 + lane, o[hh][db][e],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                float *ml = mine + kML + (wave * HW + hh) * 128 + lane;
+                __hip_atomic_store(ml, m[hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ml + 64, osum[hh][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __builtin_amdgcn_s_waitcnt(0);             // every store of this wave is complete
+            __syncthreads();                           // ... and of every wave
+            if (tid == 0) seen = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (seen == 0) return;                     // the other half merges
+        }
+        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // for the next call
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+            const float *ml = other + kML + (wave * HW + hh) * 128 + lane;
+            const float mo = __hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float lo = __hip_atomic_load(ml + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float mx = fmaxf(m[hh], mo);
+            const float a = mx == -INFINITY ? 0.f : exp2_sub(m[hh], mx);
+            const float b = mx == -INFINITY ? 0.f : exp2_sub(mo, mx);
+            const float l = osum[hh][0] * a + lo * b;
+            osum[hh] = f32x4_t{l, l, l, l};
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = __hip_atomic_load(other + (((wave * HW + hh) * DB + db) * 4 + e) * 64 + lane,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    o[hh][db][e] = o[hh][db][e] * a + x * b;
+                }
+            }
+        }
+    }
 
     const int r = r0 + j;
 #pragma unroll
@@ -1189,15 +1274,16 @@ hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
 
 template <int G, bool WIDE>
 hipError_t launch_pp(const PrefillArgs &a, hipStream_t s) {
-    const int64_t units = static_cast<int64_t>((a.num_q_tiles + kXcds - 1) / kXcds) * kXcds *
-                          a.pool.n_kv_heads * (G / 4);
+    const int n = a.num_units > 0 ? a.num_units : a.num_q_tiles;
+    const int64_t units = static_cast<int64_t>((n + kXcds - 1) / kXcds) * kXcds * a.pool.n_kv_heads * (G / 4);
     hipLaunchKernelGGL((prefill_pp_kernel<G, WIDE>), dim3(static_cast<unsigned>(units)), dim3(PpCfg::THREADS),
                        0, s, static_cast<const uint16_t *>(a.q), static_cast<uint16_t *>(a.out),
                        static_cast<const uint16_t *>(a.pool.k_layer),
                        static_cast<const uint16_t *>(a.pool.v_layer), a.pool.pool_slots,
                        a.pool.n_kv_heads, a.req_to_token, a.num_reqs, a.max_ctx_len, a.req_pool_indices,
                        a.qo_indptr, a.kv_indptr, a.q_tile_to_batch, a.q_tile_to_index, a.batch,
-                       a.total_q, a.n_heads, a.num_q_tiles, a.scale_log2);
+                       a.total_q, a.n_heads, a.num_q_tiles, a.scale_log2, a.units, a.num_units, a.num_pairs,
+                       a.part_cnt, a.part);
     return hipGetLastError();
 }
 

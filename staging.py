@@ -4,8 +4,9 @@ Used by the GPU tests and by bench.py.  It builds the page tables with the
 library's PagePool, allocates the pool with torch, places the history KV
 drawn by ``workloads`` at the slots the tables give (history stands for cache
 contents written by earlier steps), uploads the new tokens' q/k/v, and runs
-the path's calls: rope_kv_write, decode_attn, prefill_attn.  Nothing here
-computes attention or rotation itself.
+the path's calls: rope_kv_write, decode_attn, prefill_attn.  A prefill step
+carries the library's work plan unless plan=False.  Nothing here computes
+attention or rotation itself.
 """
 
 from __future__ import annotations
@@ -65,7 +66,7 @@ def build_tables(cs: Case):
     return pp, warm, reqs, cached
 
 
-def stage(cs: Case, device="cuda", canary: bool = True, threads: int = 16) -> Staged:
+def stage(cs: Case, device="cuda", canary: bool = True, threads: int = 16, plan: bool = True) -> Staged:
     dev = torch.device(device)
     dt = TORCH_DTYPE[cs.dtype]
     pp, warm, reqs, cached = build_tables(cs)
@@ -109,7 +110,8 @@ def stage(cs: Case, device="cuda", canary: bool = True, threads: int = 16) -> St
                     place(table[reqs[b], :len(kh)], kh, vh)
                     del kh, vh
     wmeta = pp.bind(reqs, cs.new_lens, cs.q_tile or 64)
-    wcache = astr.cache_from_bind(k_buffer, v_buffer, table, wmeta)
+    wcache = astr.cache_from_bind(k_buffer, v_buffer, table, wmeta,
+                                  prefill_heads=cs.n_heads if cs.kind == "prefill" and plan else None)
     pos = np.concatenate([np.arange(int(s) - int(n), int(s)) for s, n in zip(cs.seq_lens, cs.new_lens)])
     st = Staged(cs=cs, pool=pp, reqs=reqs, cached=cached, k_buffer=k_buffer, v_buffer=v_buffer,
                 freqs=astr.rope_table(cs.max_ctx_len, cs.head_dim, cs.theta, dev),

@@ -455,3 +455,91 @@ def test_decode_full_size_sampled():
     other = [l for l in range(cs.n_layers) if l != cs.layer_id][:3]
     for l in other:
         assert torch.isnan(st.k_buffer[l, :4096].float()).all()
+
+
+# ---------------------------------------------------------------------------
+# prefill work plans: split tiles merged by the half that finishes second
+# ---------------------------------------------------------------------------
+
+def _tile_steps(meta):
+    qo, kv, qt = meta["qo_indptr"], meta["kv_indptr"], meta["q_tile"]
+    out = []
+    for b, i in zip(meta["q_tile_to_batch"], meta["q_tile_to_index"]):
+        e = int(qo[b + 1] - qo[b])
+        p = int(kv[b + 1] - kv[b]) - e
+        out.append(-(-(p + int(i) * qt + min(qt, e - int(i) * qt)) // 32))
+    return out
+
+
+def _forced_plan(meta, cut, upper_first):
+    """Every tile split at key step cut(n); halves listed upper first where
+    upper_first(t) holds."""
+    rows = []
+    for t, n in enumerate(_tile_steps(meta)):
+        lo, hi = [t, 0, cut(n), 2 * t], [t, cut(n), 2 ** 31 - 1, 2 * t + 1]
+        rows += [hi, lo] if upper_first(t) else [lo, hi]
+    return np.array(rows, np.int32), meta["num_q_tiles"]
+
+
+def _with_plan(cache, units, pairs, n_heads, workspace=None):
+    import dataclasses
+    need = astr.prefill_workspace_bytes(pairs, n_heads, int(cache.k_buffer.shape[3]))
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=cache.k_buffer.device)
+    return dataclasses.replace(cache, prefill_units=torch.from_numpy(units).cuda(), num_prefill_pairs=pairs,
+                               prefill_workspace=workspace), workspace
+
+
+@pytest.mark.parametrize("name", ["cfg4", "ragged-65-129", "tiny-extends", "prefix-g8-d128",
+                                  "wide-slot-g4-kv64-d128"])
+def test_prefill_forced_split_matches_oracle(name):
+    cs = PREFILL[name]()
+    st = staging.stage(cs, plan=False)
+    staging.run_write(st)
+    want = E.expected_prefill(cs)
+    off = E.new_offsets(cs)
+    meta = st.attn_meta
+    variants = [
+        ("half, lower first", lambda n: n // 2, lambda t: False),
+        ("half, upper first", lambda n: n // 2, lambda t: True),
+        ("one step, alternating", lambda n: min(1, n), lambda t: t % 2 == 1),
+        ("empty lower half", lambda n: 0, lambda t: t % 3 == 0),
+        ("empty upper half", lambda n: n + 3, lambda t: t % 2 == 0),
+    ]
+    ws = None
+    for label, cut, upper in variants:
+        units, pairs = _forced_plan(meta, cut, upper)
+        cache, ws = _with_plan(st.attn_cache, units, pairs, cs.n_heads, ws)
+        for rep in range(2):                    # the counts are left at zero for the next call
+            say(f"prefill forced split case={name} {label} call {rep}")
+            out = astr.prefill_attn(st.q, cache, cs.layer_id)
+            torch.cuda.synchronize()
+            got = to_np(out)
+            for b in range(cs.batch):
+                E.assert_close(got[off[b]:off[b + 1]], want[b], cs.dtype, f"{name} {label} request {b}")
+        slots = pairs * cs.n_heads // 4
+        counts = ws[:4 * slots].view(torch.int32)
+        assert int(counts.abs().sum()) == 0, "completion counts must be zero after a call"
+
+
+@pytest.mark.parametrize("name", ["cfg4", "cfg4-seed101", "cfg3", "prefix-g8-d128"])
+def test_prefill_plan_matches_unplanned(name):
+    cs = PREFILL[name]()
+    st = staging.stage(cs)
+    staging.run_write(st)
+    c = st.attn_cache
+    say(f"prefill library plan case={name} units={0 if c.prefill_units is None else len(c.prefill_units)} "
+        f"pairs={c.num_prefill_pairs}")
+    planned = staging.run_prefill(st)
+    import dataclasses
+    plain = astr.prefill_attn(st.q, dataclasses.replace(c, prefill_units=None, num_prefill_pairs=0,
+                                                        prefill_workspace=None), cs.layer_id)
+    torch.cuda.synchronize()
+    want = E.expected_prefill(cs)
+    off = E.new_offsets(cs)
+    a, b_ = to_np(planned), to_np(plain)
+    for b in range(cs.batch):
+        E.assert_close(a[off[b]:off[b + 1]], want[b], cs.dtype, f"{name} planned request {b}")
+        E.assert_close(b_[off[b]:off[b + 1]], want[b], cs.dtype, f"{name} unplanned request {b}")
+    # the two differ only in the order of the softmax sums
+    assert np.linalg.norm(a - b_) <= 2e-3 * np.linalg.norm(b_)

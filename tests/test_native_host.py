@@ -368,3 +368,174 @@ def test_decode_split_items_errors_and_abi_checks():
     assert b"split_chunk 32" in so.astr_last_error()
     m.split_item_chunk, m.num_split_items = 64, 0        # no count
     assert so.astr_decode_attn(q, q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, None) == L.ASTR_E_INVAL
+
+
+# ---------------------------------------------------------------------------
+# prefill work plan
+# ---------------------------------------------------------------------------
+
+def _plan_meta(seq, ext, q_tile=64):
+    """Host step metadata of a ragged prefill (tiles heaviest first, as the
+    builder lists them)."""
+    seq, ext = np.asarray(seq), np.asarray(ext)
+    kv = np.concatenate([[0], np.cumsum(seq)]).astype(np.int32)
+    qo = np.concatenate([[0], np.cumsum(ext)]).astype(np.int32)
+    tiles = sorted((-(int(seq[b] - ext[b]) + min(q_tile * (i + 1), int(ext[b]))), b, i)
+                   for b in range(len(seq)) for i in range(-(-int(ext[b]) // q_tile)))
+    return dict(qo_indptr=qo, kv_indptr=kv, q_tile_to_batch=np.array([t[1] for t in tiles], np.int32),
+                q_tile_to_index=np.array([t[2] for t in tiles], np.int32), num_q_tiles=len(tiles),
+                q_tile=q_tile)
+
+
+def _plan_rule(meta, wg, num_cus):
+    """The prefill work plan stated as its documented rule, in Python."""
+    qo, kv = meta["qo_indptr"], meta["kv_indptr"]
+    qt = meta["q_tile"]
+    steps = []
+    for b, i in zip(meta["q_tile_to_batch"], meta["q_tile_to_index"]):
+        e = int(qo[b + 1] - qo[b])
+        p = int(kv[b + 1] - kv[b]) - e
+        row0 = int(i) * qt
+        steps.append(-(-(p + row0 + min(qt, e - row0)) // 32) if (e > 0 and p >= 0 and row0 < e) else 0)
+    big = 2 ** 31 - 1
+
+    def units(thr):
+        out = []
+        for t, n in enumerate(steps):
+            if n >= 2 and n > thr:
+                h = n // 2
+                out += [(8.5 + h, t, 0, 0, h), (9.5 + n - h, t, 1, h, big)]
+            else:
+                out.append((7.0 + n if n > 0 else 0.1, t, -1, 0, big))
+        return sorted(out, key=lambda u: (-u[0], u[1], u[2]))
+
+    def deal(lst):
+        free = [[0.0] * (num_cus // 8) for _ in range(8)]
+        queue = [[] for _ in range(8)]
+        end = 0.0
+        w = min(wg, num_cus // 8)
+        for u in lst:
+            x = min(range(8), key=lambda x: (sorted(free[x])[w - 1] + u[0], len(queue[x]), x))
+            for _ in range(wg):
+                f = sorted(free[x])
+                f[0] += u[0]
+                end = max(end, f[0])
+                free[x] = f
+            queue[x].append(u)
+        return end, queue
+
+    base, queue = deal(units(big))
+    mx = max(steps) if steps else 0
+    best_end, best_q = base, None
+    for k in range(9, 2, -1):
+        e, q = deal(units(mx * k // 10))
+        if e < best_end:
+            best_end, best_q = e, q
+    if best_q is not None and best_end <= 0.90 * base:
+        queue = best_q
+    pair_of, rows = {}, []
+    for k in range(max(len(q) for q in queue)):
+        for x in range(8):
+            if k >= len(queue[x]):
+                rows.append([-1, 0, 0, -1])
+                continue
+            u = queue[x][k]
+            pw = -1
+            if u[2] >= 0:
+                pair_of.setdefault(u[1], len(pair_of))
+                pw = 2 * pair_of[u[1]] + u[2]
+            rows.append([u[1], u[3], u[4], pw])
+    return np.array(rows, np.int32).reshape(-1, 4), len(pair_of)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_prefill_plan_follows_the_rule(seed):
+    import paged_gqa_attention_rope_amd as astr
+    _lib()
+    rng = np.random.default_rng(seed)
+    shapes = [
+        (rng.integers(0, 129, 16) * 16, rng.integers(32, 513, 16)),     # radix prefixes, mixed extends
+        (np.full(64, 2048), np.full(64, 64)),                           # balanced
+        (np.zeros(4, int), rng.integers(64, 1025, 4)),                  # few long prompts
+        (rng.integers(0, 40, 7), rng.integers(1, 4, 7)),                # tiny
+    ]
+    for pre, ext in shapes:
+        meta = _plan_meta(np.asarray(pre) + np.asarray(ext), ext)
+        for wg, cus in ((4, 256), (2, 256), (4, 64)):
+            units, pairs = astr.prefill_plan(meta, 4 * wg, cus)
+            want, want_pairs = _plan_rule(meta, wg, cus)
+            assert np.array_equal(units, want) and pairs == want_pairs
+            # every tile once whole, or twice as halves [0, h) and [h, end)
+            assert len(units) % 8 == 0
+            seen = {}
+            for t, lo, hi, pw in units.tolist():
+                if t == -1:
+                    assert (lo, hi, pw) == (0, 0, -1)      # padding
+                    continue
+                seen.setdefault(t, []).append((lo, hi, pw))
+            assert sorted(seen) == list(range(meta["num_q_tiles"]))
+            for t, us in seen.items():
+                if len(us) == 1:
+                    assert us[0] == (0, 2 ** 31 - 1, -1)
+                else:
+                    (lo0, hi0, p0), (lo1, hi1, p1) = sorted(us)
+                    assert lo0 == 0 and hi0 == lo1 > 0 and hi1 == 2 ** 31 - 1
+                    assert p0 // 2 == p1 // 2 and p0 % 2 == 0 and p1 % 2 == 1
+            assert sorted({pw // 2 for *_, pw in units.tolist() if pw >= 0}) == list(range(pairs))
+
+
+def test_prefill_plan_splits_only_what_dominates():
+    import paged_gqa_attention_rope_amd as astr
+    _lib()
+    # balanced: no split
+    units, pairs = astr.prefill_plan(_plan_meta(np.full(64, 2112), np.full(64, 64)), 16)
+    assert pairs == 0 and len(units) == 64 and (units[:, 0] >= 0).all()
+    # one long tile among many short ones: split
+    seq = np.concatenate([[2560], np.full(300, 200)])
+    ext = np.concatenate([[64], np.full(300, 64)])
+    units, pairs = astr.prefill_plan(_plan_meta(seq, ext), 16)
+    assert pairs == 1 and units[0][0] == 0 and units[1][0] == 0     # both halves first, on XCDs 0 and 1
+    assert astr.prefill_workspace_bytes(0, 16, 128) == 0
+    per = 2 * (8 * 2 * 8 * 64 * 4 + 8 * 2 * 64 * 2) * 4
+    assert astr.prefill_workspace_bytes(3, 16, 128) == 256 + 12 * per
+    assert astr.prefill_workspace_bytes(-1, 16, 128) == 0
+
+
+def test_prefill_plan_errors_and_abi_checks():
+    import paged_gqa_attention_rope_amd as astr
+    L = _lib()
+    so = L.lib()
+    meta = _plan_meta([100, 300], [50, 200])
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    n, pr = ctypes.c_int(), ctypes.c_int()
+    u = np.zeros((8, 4), np.int32)
+    args = [p(meta["qo_indptr"]), p(meta["kv_indptr"]), 2, p(meta["q_tile_to_batch"]),
+            p(meta["q_tile_to_index"]), meta["num_q_tiles"], 64]
+    assert so.astr_prefill_plan(*args, 4, 256, p(u), 8, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_OK
+    assert so.astr_prefill_plan(*args, 4, 4, p(u), 8, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
+    assert so.astr_prefill_plan(*args, 0, 256, p(u), 8, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
+    assert so.astr_prefill_plan(*args, 4, 256, p(u), 7, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
+    # the prefill call checks the plan before anything is launched
+    m = L.KvMeta()
+    m.k_buffer = m.v_buffer = 0x1000
+    m.pool_slots, m.n_layers, m.n_kv_heads, m.head_dim, m.kv_dtype = 1024, 1, 4, 128, L.ASTR_BF16
+    m.req_to_token = m.req_pool_indices = m.kv_indptr = m.qo_indptr = 0x4000
+    m.q_tile_to_batch = m.q_tile_to_index = 0x4000
+    m.num_reqs, m.max_ctx_len, m.batch, m.max_len, m.num_q_tiles, m.q_tile = 2, 512, 2, 300, 5, 64
+    q = ctypes.c_void_p(0x2000)
+
+    def call():
+        return so.astr_prefill_attn(q, q, 250, 16, ctypes.byref(m), 0, 0.0, None)
+
+    m.prefill_units = 0x8000                             # no count
+    assert call() == L.ASTR_E_INVAL and b"incomplete" in so.astr_last_error()
+    m.num_prefill_units, m.prefill_units = 6, 0x8004     # misaligned
+    assert call() == L.ASTR_E_INVAL and b"aligned" in so.astr_last_error()
+    m.prefill_units, m.num_prefill_pairs = 0x8000, 1     # pairs without workspace
+    assert call() == L.ASTR_E_INVAL and b"workspace" in so.astr_last_error()
+    m.prefill_workspace = 0x9000
+    m.prefill_workspace_bytes = astr.prefill_workspace_bytes(1, 16, 128) - 1
+    assert call() == L.ASTR_E_INVAL and b"needs" in so.astr_last_error()
+    m.prefill_workspace_bytes += 1
+    m.num_prefill_units = 81                             # more than 16 * num_q_tiles
+    assert call() == L.ASTR_E_INVAL and b"too large" in so.astr_last_error()
