@@ -100,8 +100,10 @@ typedef struct astr_kv_meta {
      * (a pair) each leave their unnormalised partial result in the
      * workspace, and the one that finishes second merges both.  16-byte
      * aligned device array. */
-    const int32_t *prefill_units;     /* [num_prefill_units][4]: tile, step_lo, step_hi,
-                                         2 * pair + (0 lower keys, 1 upper keys), or -1 */
+    const int32_t *prefill_units;     /* [num_prefill_units][8]: tile, step_lo, step_hi,
+                                         2 * pair + (0 lower keys, 1 upper keys) or -1,
+                                         then the tile's request row, first query row,
+                                         rows (0: nothing to do) and first row's position */
     int32_t num_prefill_units;        /* host: 0 = one unit per tile, in tile order */
     int32_t num_prefill_pairs;        /* host: split tiles in the plan */
     void *prefill_workspace;          /* device, zeroed before its first use */
@@ -329,19 +331,24 @@ size_t astr_prefill_workspace_bytes(int pairs, int n_heads, int head_dim);
  * on the ones free first.  The split set with the earliest simulated end
  * wins if it ends at least 10% before the unsplit list.  Entry 8k + x of the
  * plan is the k-th unit of XCD x (the kernel runs unit u on XCD u % 8);
- * shorter queues are padded with units of tile -1, which do nothing.
- *   qo_indptr, kv_indptr  host [batch + 1]; q_tile_to_batch, q_tile_to_index
- *   host [num_q_tiles]; q_tile rows per tile (64); workgroups_per_tile
- *   = n_heads / 4 for the kernel that follows plans; num_cus >= 8
- *   units       host [capacity][4], written (layout of astr_kv_meta.prefill_units)
+ * shorter queues are padded with units of tile -1 and 0 rows, which do
+ * nothing.
+ * A unit also carries its tile's request row req_pool_indices[b], first
+ * query row qo_indptr[b] + row0, rows and first row's position p_b + row0,
+ * so that the kernel reads one descriptor instead of the tile maps.
+ *   qo_indptr, kv_indptr  host [batch + 1]; req_pool_indices host [batch];
+ *   q_tile_to_batch, q_tile_to_index host [num_q_tiles]; q_tile rows per
+ *   tile (64); workgroups_per_tile = n_heads / 4 for the kernel that follows
+ *   plans; num_cus >= 8
+ *   units       host [capacity][8], written (layout of astr_kv_meta.prefill_units)
  *   *num_units, *num_pairs  written
  * capacity >= 16 * num_q_tiles always suffices.
  * Errors: INVAL (null pointer, negative size, num_cus < 8, capacity short).
  */
-int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_indptr, int batch,
-                      const int32_t *q_tile_to_batch, const int32_t *q_tile_to_index, int num_q_tiles,
-                      int q_tile, int workgroups_per_tile, int num_cus, int32_t *units, int capacity,
-                      int *num_units, int *num_pairs);
+int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_indptr, const int32_t *req_pool_indices,
+                      int batch, const int32_t *q_tile_to_batch, const int32_t *q_tile_to_index,
+                      int num_q_tiles, int q_tile, int workgroups_per_tile, int num_cus, int32_t *units,
+                      int capacity, int *num_units, int *num_pairs);
 
 /* ------------------------------------------------------------------------ */
 /* Page-table builder (host only; no device calls)                          */

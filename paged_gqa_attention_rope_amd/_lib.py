@@ -75,7 +75,7 @@ def lib():
                                     ctypes.c_float, c_vp]
     L.astr_prefill_workspace_bytes.argtypes = [c_int, c_int, c_int]
     L.astr_prefill_workspace_bytes.restype = ctypes.c_size_t
-    L.astr_prefill_plan.argtypes = [c_i32p, c_i32p, c_int, c_i32p, c_i32p, c_int, c_int, c_int, c_int,
+    L.astr_prefill_plan.argtypes = [c_i32p, c_i32p, c_i32p, c_int, c_i32p, c_i32p, c_int, c_int, c_int, c_int,
                                     c_i32p, c_int, ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
     L.astr_pagepool_create.argtypes = [ctypes.POINTER(c_vp), c_int, ctypes.c_int64, c_int, c_int,
                                        c_int, c_i32p]

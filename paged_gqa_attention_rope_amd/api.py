@@ -76,7 +76,7 @@ class KVCache:
     split_item_index: Optional[torch.Tensor] = None
     num_split_items: int = 0
     split_item_chunk: int = 0
-    # prefill work plan ([n, 4] int32 units) and its workspace; optional
+    # prefill work plan ([n, 8] int32 units) and its workspace; optional
     prefill_units: Optional[torch.Tensor] = None
     num_prefill_pairs: int = 0
     prefill_workspace: Optional[torch.Tensor] = None
@@ -102,15 +102,17 @@ def decode_split_items(seq_lens, split_chunk: int):
 
 def prefill_plan(meta: dict, n_heads: int, num_cus: int = 256):
     """Host prefill work plan of a bound step (astr_prefill_plan) for a model
-    with n_heads query heads; returns ([n, 4] int32 units, number of pairs)."""
+    with n_heads query heads; returns ([n, 8] int32 units, number of pairs)."""
     _need(n_heads >= 4, "the prefill plan is for 4 or more query heads")
     nt = int(meta["num_q_tiles"])
     qo, kv = _i32(meta["qo_indptr"]), _i32(meta["kv_indptr"])
+    rpi = _i32(meta["req_pool_indices"])
+    _need(rpi.size == qo.size - 1, "req_pool_indices must have one entry per batch entry")
     t2b, t2i = _i32(meta["q_tile_to_batch"])[:nt], _i32(meta["q_tile_to_index"])[:nt]
     cap = max(16 * nt, 8)
-    units = np.zeros((cap, 4), np.int32)
+    units = np.zeros((cap, 8), np.int32)
     n, pairs = ctypes.c_int(), ctypes.c_int()
-    check(lib().astr_prefill_plan(_i32p(qo), _i32p(kv), int(qo.size) - 1, _i32p(t2b), _i32p(t2i), nt,
+    check(lib().astr_prefill_plan(_i32p(qo), _i32p(kv), _i32p(rpi), int(qo.size) - 1, _i32p(t2b), _i32p(t2i), nt,
                                   int(meta["q_tile"]), int(n_heads) // 4, int(num_cus), _i32p(units), cap,
                                   ctypes.byref(n), ctypes.byref(pairs)))
     return units[:n.value].copy(), pairs.value
@@ -186,7 +188,7 @@ def _meta(c: KVCache, need_prefill: bool = False) -> KvMeta:
         m.num_split_items, m.split_item_chunk = int(c.num_split_items), int(c.split_item_chunk)
     if need_prefill and c.prefill_units is not None:
         _dev_tensor(c.prefill_units, "prefill_units", torch.int32, kb.device)
-        _need(c.prefill_units.dim() == 2 and c.prefill_units.shape[1] == 4, "prefill_units must be [n, 4]")
+        _need(c.prefill_units.dim() == 2 and c.prefill_units.shape[1] == 8, "prefill_units must be [n, 8]")
         m.prefill_units = c.prefill_units.data_ptr()
         m.num_prefill_units, m.num_prefill_pairs = int(c.prefill_units.shape[0]), int(c.num_prefill_pairs)
         if c.prefill_workspace is not None:

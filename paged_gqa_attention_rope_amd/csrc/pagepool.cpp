@@ -19,6 +19,7 @@
 // all when evicting every evictable page would still leave it short.
 #include <cstdint>
 #include <algorithm>
+#include <array>
 #include <cstring>
 #include <new>
 #include <set>
@@ -632,16 +633,19 @@ double deal(const std::vector<PlanUnit> &list, int wg_per_unit, int cus_per_xcd,
 
 }  // namespace
 
-extern "C" int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_indptr, int batch,
-                                 const int32_t *q_tile_to_batch, const int32_t *q_tile_to_index,
-                                 int num_q_tiles, int q_tile, int workgroups_per_tile, int num_cus,
-                                 int32_t *units, int capacity, int *num_units, int *num_pairs) {
-    if (!qo_indptr || !kv_indptr || !num_units || !num_pairs || batch < 0 || num_q_tiles < 0 ||
+extern "C" int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                 const int32_t *req_pool_indices, int batch, const int32_t *q_tile_to_batch,
+                                 const int32_t *q_tile_to_index, int num_q_tiles, int q_tile,
+                                 int workgroups_per_tile, int num_cus, int32_t *units, int capacity,
+                                 int *num_units, int *num_pairs) {
+    if (!qo_indptr || !kv_indptr || !req_pool_indices || !num_units || !num_pairs || batch < 0 || num_q_tiles < 0 ||
         q_tile < 1 || workgroups_per_tile < 1 || num_cus < kPlanXcds || capacity < 0 ||
         (num_q_tiles > 0 && (!q_tile_to_batch || !q_tile_to_index || !units)))
         return astr::fail(ASTR_E_INVAL, "prefill_plan: bad argument");
-    // key steps seen by each tile (0 for a tile the kernel skips)
+    // key steps seen by each tile (0 for a tile the kernel skips), and its
+    // request row, first query row, rows and first row's position
     std::vector<int> steps(num_q_tiles, 0);
+    std::vector<std::array<int32_t, 4>> rows_of(num_q_tiles, {0, 0, 0, 0});
     int max_steps = 0;
     for (int t = 0; t < num_q_tiles; ++t) {
         const int b = q_tile_to_batch[t];
@@ -651,8 +655,13 @@ extern "C" int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_ind
         const int64_t p = static_cast<int64_t>(kv_indptr[b + 1]) - kv_indptr[b] - e;
         const int64_t row0 = idx * q_tile;
         if (e <= 0 || p < 0 || row0 >= e) continue;
-        const int64_t kv_end = p + row0 + std::min<int64_t>(q_tile, e - row0);
-        steps[t] = static_cast<int>(std::min<int64_t>((kv_end + kPlanStep - 1) / kPlanStep, INT32_MAX / 2));
+        const int64_t rows = std::min<int64_t>(q_tile, e - row0);
+        const int64_t kv_end = p + row0 + rows;
+        const int64_t q_row = qo_indptr[b] + row0;
+        if (kv_end > INT32_MAX || q_row > INT32_MAX) continue;
+        steps[t] = static_cast<int>((kv_end + kPlanStep - 1) / kPlanStep);
+        rows_of[t] = {req_pool_indices[b], static_cast<int32_t>(q_row), static_cast<int32_t>(rows),
+                      static_cast<int32_t>(p + row0)};
         max_steps = std::max(max_steps, steps[t]);
     }
     const int cus_per_xcd = num_cus / kPlanXcds;
@@ -686,9 +695,10 @@ extern "C" int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_ind
     int pairs = 0;
     for (size_t k = 0; k < len; ++k) {
         for (int x = 0; x < kPlanXcds; ++x) {
-            int32_t *row = units + 4 * (kPlanXcds * k + x);
+            int32_t *row = units + 8 * (kPlanXcds * k + x);
             if (k >= queue[x].size()) {
                 row[0] = -1, row[1] = 0, row[2] = 0, row[3] = -1;
+                row[4] = row[5] = row[6] = row[7] = 0;
                 continue;
             }
             const PlanUnit &u = best[queue[x][k]];
@@ -698,6 +708,7 @@ extern "C" int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_ind
                 pw = 2 * pair_of[u.tile] + u.piece;
             }
             row[0] = u.tile, row[1] = u.lo, row[2] = u.hi, row[3] = pw;
+            for (int f = 0; f < 4; ++f) row[4 + f] = rows_of[u.tile][f];
         }
     }
     *num_units = static_cast<int>(n);

@@ -809,21 +809,33 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     const int u = k_in % units_per_tile;
     const int kvh = u / GROUPS;
     const int hg = u % GROUPS;
-    int tile = unit, step_lo = 0, step_hi = INT_MAX, pw = -1;
-    if (num_units > 0) {
-        if (unit >= num_units) return;
-        const int4 d = reinterpret_cast<const int4 *>(units)[unit];
-        tile = d.x;
-        step_lo = d.y;
-        step_hi = d.z;
-        pw = d.w < 0 ? -1 : d.w;
-        if (step_lo < 0 || pw >= 2 * num_pairs) return;     // not a plan's unit
-    }
-    if (tile < 0 || tile >= num_q_tiles) return;
+    int step_lo = 0, step_hi = INT_MAX, pw = -1;
     TileInfo ti;
-    if (!tile_info(tile, q_tile_to_batch, q_tile_to_index, qo_indptr, kv_indptr,
-                   req_pool_indices, batch, num_reqs, max_ctx_len, total_q, TQ, ti))
-        return;
+    if (num_units > 0) {
+        // the plan states the unit's rows and keys: one load, where the tile
+        // maps would take two dependent ones
+        if (unit >= num_units) return;
+        const int4 d0 = reinterpret_cast<const int4 *>(units)[2 * unit];
+        const int4 d1 = reinterpret_cast<const int4 *>(units)[2 * unit + 1];
+        step_lo = d0.y;
+        step_hi = d0.z;
+        pw = d0.w < 0 ? -1 : d0.w;
+        ti.req = d1.x;
+        ti.q0 = d1.y;
+        ti.row0 = 0;
+        ti.rows = d1.z;
+        ti.p = d1.w;
+        if (step_lo < 0 || pw >= 2 * num_pairs || ti.rows < 1 || ti.rows > TQ || ti.req < 0 ||
+            ti.req >= num_reqs || ti.q0 < 0 || ti.q0 > total_q - ti.rows || ti.p < 0 ||
+            ti.p > max_ctx_len - ti.rows)
+            return;                                    // not a unit of a plan for this call
+        ti.kv_end = ti.p + ti.rows;
+    } else {
+        if (unit >= num_q_tiles ||
+            !tile_info(unit, q_tile_to_batch, q_tile_to_index, qo_indptr, kv_indptr, req_pool_indices,
+                       batch, num_reqs, max_ctx_len, total_q, TQ, ti))
+            return;
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -474,9 +474,14 @@ def _tile_steps(meta):
 def _forced_plan(meta, cut, upper_first):
     """Every tile split at key step cut(n); halves listed upper first where
     upper_first(t) holds."""
+    qo, kv, rpi = meta["qo_indptr"], meta["kv_indptr"], meta["req_pool_indices"]
     rows = []
     for t, n in enumerate(_tile_steps(meta)):
-        lo, hi = [t, 0, cut(n), 2 * t], [t, cut(n), 2 ** 31 - 1, 2 * t + 1]
+        b, i = int(meta["q_tile_to_batch"][t]), int(meta["q_tile_to_index"][t])
+        e = int(qo[b + 1] - qo[b])
+        p = int(kv[b + 1] - kv[b]) - e
+        desc = [int(rpi[b]), int(qo[b]) + 64 * i, min(64, e - 64 * i), p + 64 * i]
+        lo, hi = [t, 0, cut(n), 2 * t] + desc, [t, cut(n), 2 ** 31 - 1, 2 * t + 1] + desc
         rows += [hi, lo] if upper_first(t) else [lo, hi]
     return np.array(rows, np.int32), meta["num_q_tiles"]
 

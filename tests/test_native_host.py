@@ -384,19 +384,21 @@ def _plan_meta(seq, ext, q_tile=64):
                    for b in range(len(seq)) for i in range(-(-int(ext[b]) // q_tile)))
     return dict(qo_indptr=qo, kv_indptr=kv, q_tile_to_batch=np.array([t[1] for t in tiles], np.int32),
                 q_tile_to_index=np.array([t[2] for t in tiles], np.int32), num_q_tiles=len(tiles),
-                q_tile=q_tile)
+                q_tile=q_tile, req_pool_indices=(np.arange(len(seq)) * 7 + 3).astype(np.int32))
 
 
 def _plan_rule(meta, wg, num_cus):
     """The prefill work plan stated as its documented rule, in Python."""
-    qo, kv = meta["qo_indptr"], meta["kv_indptr"]
+    qo, kv, rpi = meta["qo_indptr"], meta["kv_indptr"], meta["req_pool_indices"]
     qt = meta["q_tile"]
-    steps = []
+    steps, rows_of = [], []
     for b, i in zip(meta["q_tile_to_batch"], meta["q_tile_to_index"]):
         e = int(qo[b + 1] - qo[b])
         p = int(kv[b + 1] - kv[b]) - e
         row0 = int(i) * qt
-        steps.append(-(-(p + row0 + min(qt, e - row0)) // 32) if (e > 0 and p >= 0 and row0 < e) else 0)
+        ok = e > 0 and p >= 0 and row0 < e
+        steps.append(-(-(p + row0 + min(qt, e - row0)) // 32) if ok else 0)
+        rows_of.append([int(rpi[b]), int(qo[b]) + row0, min(qt, e - row0), p + row0] if ok else [0, 0, 0, 0])
     big = 2 ** 31 - 1
 
     def units(thr):
@@ -437,15 +439,15 @@ def _plan_rule(meta, wg, num_cus):
     for k in range(max(len(q) for q in queue)):
         for x in range(8):
             if k >= len(queue[x]):
-                rows.append([-1, 0, 0, -1])
+                rows.append([-1, 0, 0, -1, 0, 0, 0, 0])
                 continue
             u = queue[x][k]
             pw = -1
             if u[2] >= 0:
                 pair_of.setdefault(u[1], len(pair_of))
                 pw = 2 * pair_of[u[1]] + u[2]
-            rows.append([u[1], u[3], u[4], pw])
-    return np.array(rows, np.int32).reshape(-1, 4), len(pair_of)
+            rows.append([u[1], u[3], u[4], pw] + rows_of[u[1]])
+    return np.array(rows, np.int32).reshape(-1, 8), len(pair_of)
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
@@ -468,11 +470,17 @@ def test_prefill_plan_follows_the_rule(seed):
             # every tile once whole, or twice as halves [0, h) and [h, end)
             assert len(units) % 8 == 0
             seen = {}
-            for t, lo, hi, pw in units.tolist():
+            for t, lo, hi, pw, *rest in units.tolist():
                 if t == -1:
-                    assert (lo, hi, pw) == (0, 0, -1)      # padding
+                    assert (lo, hi, pw, *rest) == (0, 0, -1, 0, 0, 0, 0)      # padding
                     continue
                 seen.setdefault(t, []).append((lo, hi, pw))
+                # the tile's rows and keys, as its maps give them
+                b, i = meta["q_tile_to_batch"][t], meta["q_tile_to_index"][t]
+                e = meta["qo_indptr"][b + 1] - meta["qo_indptr"][b]
+                pre = meta["kv_indptr"][b + 1] - meta["kv_indptr"][b] - e
+                assert rest == [meta["req_pool_indices"][b], meta["qo_indptr"][b] + 64 * i,
+                                min(64, e - 64 * i), pre + 64 * i]
             assert sorted(seen) == list(range(meta["num_q_tiles"]))
             for t, us in seen.items():
                 if len(us) == 1:
@@ -481,7 +489,7 @@ def test_prefill_plan_follows_the_rule(seed):
                     (lo0, hi0, p0), (lo1, hi1, p1) = sorted(us)
                     assert lo0 == 0 and hi0 == lo1 > 0 and hi1 == 2 ** 31 - 1
                     assert p0 // 2 == p1 // 2 and p0 % 2 == 0 and p1 % 2 == 1
-            assert sorted({pw // 2 for *_, pw in units.tolist() if pw >= 0}) == list(range(pairs))
+            assert sorted({u[3] // 2 for u in units.tolist() if u[3] >= 0}) == list(range(pairs))
 
 
 def test_prefill_plan_splits_only_what_dominates():
@@ -508,9 +516,9 @@ def test_prefill_plan_errors_and_abi_checks():
     meta = _plan_meta([100, 300], [50, 200])
     p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     n, pr = ctypes.c_int(), ctypes.c_int()
-    u = np.zeros((8, 4), np.int32)
-    args = [p(meta["qo_indptr"]), p(meta["kv_indptr"]), 2, p(meta["q_tile_to_batch"]),
-            p(meta["q_tile_to_index"]), meta["num_q_tiles"], 64]
+    u = np.zeros((8, 8), np.int32)
+    args = [p(meta["qo_indptr"]), p(meta["kv_indptr"]), p(meta["req_pool_indices"]), 2,
+            p(meta["q_tile_to_batch"]), p(meta["q_tile_to_index"]), meta["num_q_tiles"], 64]
     assert so.astr_prefill_plan(*args, 4, 256, p(u), 8, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_OK
     assert so.astr_prefill_plan(*args, 4, 4, p(u), 8, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
     assert so.astr_prefill_plan(*args, 0, 256, p(u), 8, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
