@@ -294,11 +294,15 @@ def main():
     t0 = time.perf_counter()
     st_d.pool.bind(st_d.reqs, np.ones(cs_d.batch, dtype=np.int32), 64)
     bind_ms = (time.perf_counter() - t0) * 1e3
+    # and of the prefill work plan (built once per step, shared by all layers)
+    import paged_gqa_attention_rope_amd as astr
+    t0 = time.perf_counter()
+    astr.prefill_plan(st_p.attn_meta, cs_p.n_heads, torch.cuda.get_device_properties(dev).multi_processor_count)
+    plan_ms = (time.perf_counter() - t0) * 1e3
 
     q_dec = staging.decode_query(st_d)
     q_unrot = q_dec.clone()                     # the fused decode takes q before rotation
     out_d = torch.empty_like(q_dec)
-    import paged_gqa_attention_rope_amd as astr
     o_part, lse_part = astr.decode_workspace(st_d.attn_cache, cs_d.n_heads, cs_d.split_chunk)
     out_p = torch.empty_like(st_p.q)
     stream = torch.cuda.current_stream()
@@ -381,10 +385,13 @@ def main():
                                  "frac": round(pre_tfs / BF16_PEAK_TFLOPS, 4),
                                  "traffic": measured_traffic("prefill"),
                                  "kernel": "prefill_attn", "flops_per_launch": pflops,
-                                 "ms_per_launch": round(float(t_pre), 5)}},
+                                 "ms_per_launch": round(float(t_pre), 5)},
+                    "plan": {"units": 0 if st_p.attn_cache.prefill_units is None
+                             else int(st_p.attn_cache.prefill_units.shape[0]),
+                             "split_tiles": int(st_p.attn_cache.num_prefill_pairs)}},
         "parts_ms": {"rope_kv_write_decode": round(float(t_wd), 5), "decode_attn": round(float(t_dec), 5),
                      "rope_kv_write_prefill": round(float(t_wp), 5), "prefill_attn": round(float(t_pre), 5),
-                     "host_bind_decode": round(bind_ms, 3)},
+                     "host_bind_decode": round(bind_ms, 3), "host_plan_prefill": round(plan_ms, 3)},
         "next": nxt,
         "cpu_baseline": cpu,
     }

@@ -321,15 +321,18 @@ size_t astr_prefill_workspace_bytes(int pairs, int n_heads, int head_dim);
  * steps of 32 keys (measured on MI355X: ~1 us per step, ~5 us of prologue,
  * ~2 us to store a tile's output, ~3 us to publish a half's state, ~3 us to
  * merge): a whole tile 7 + n_t (0.1 when skipped), a lower half [0, h) 8.5
- * + h, an upper half [h, end) 9.5 + n_t - h, h = n_t / 2.  For each split
- * set {t : n_t >= 2, n_t > T}, T = floor(max_t n_t * k / 10), k = 9 .. 3,
- * and for no split, the units are listed by decreasing cost (ties: tile
+ * + h, an upper half [h, end) 9.5 + n_t - h.  Candidates: no split; the
+ * tiles with n_t > floor(max_t n_t * k / 10), k = 9 .. 3, cut at h =
+ * n_t / 2; the N longest tiles (ties: tile order), N in {1, 2, 3, 4, 5, 6,
+ * 8, 10, 12, 16} below num_q_tiles, cut at h = max(1, floor(3 n_t / 10))
+ * (only tiles with n_t >= 2 are cut).  For each, the units are listed by decreasing cost (ties: tile
  * order, then lower half first) and dealt to the 8 XCDs in that order, each
  * to the XCD where it would end first (ties: fewer units queued, then the
  * lower XCD); an XCD runs its queue in order on num_cus / 8 compute units,
  * one workgroup per compute unit, the unit's workgroups_per_tile workgroups
- * on the ones free first.  The split set with the earliest simulated end
- * wins if it ends at least 10% before the unsplit list.  Entry 8k + x of the
+ * on the ones free first.  The candidate with the earliest simulated end
+ * (the first listed on ties) wins if it ends at least 10% before the
+ * unsplit list.  Entry 8k + x of the
  * plan is the k-th unit of XCD x (the kernel runs unit u on XCD u % 8);
  * shorter queues are padded with units of tile -1 and 0 rows, which do
  * nothing.

@@ -571,15 +571,16 @@ struct PlanUnit {
     int lo, hi;                            // key steps [lo, hi)
 };
 
-// Units of the tiles, those with more than `thr` steps split in two halves,
-// by decreasing cost (ties: tile order, then lower half first).
-std::vector<PlanUnit> plan_units(const std::vector<int> &steps, int thr) {
+// Units of the tiles, those marked in `split` cut in two halves at h =
+// max(1, floor(n * num / den)) steps, by decreasing cost (ties: tile order,
+// then lower half first).
+std::vector<PlanUnit> plan_units(const std::vector<int> &steps, const std::vector<char> &split, int num, int den) {
     std::vector<PlanUnit> list;
     list.reserve(2 * steps.size());
     for (int t = 0; t < static_cast<int>(steps.size()); ++t) {
         const int n = steps[t];
-        if (n >= 2 && n > thr) {
-            const int h = n / 2;
+        if (split[t] && n >= 2) {
+            const int h = std::max(1, static_cast<int>(static_cast<int64_t>(n) * num / den));
             list.push_back({kLower + h, t, 0, 0, h});
             list.push_back({kUpper + (n - h), t, 1, h, INT32_MAX});
         } else {
@@ -601,30 +602,34 @@ std::vector<PlanUnit> plan_units(const std::vector<int> &steps, int thr) {
 // Returns the simulated end; queue[x] receives the units of XCD x.
 double deal(const std::vector<PlanUnit> &list, int wg_per_unit, int cus_per_xcd,
             std::vector<std::vector<int>> &queue) {
-    std::vector<std::multiset<double>> free_at(kPlanXcds);
-    for (auto &f : free_at)
-        for (int c = 0; c < cus_per_xcd; ++c) f.insert(0.0);
+    // free times of each XCD's compute units, ascending
+    std::vector<std::vector<double>> free_at(kPlanXcds, std::vector<double>(cus_per_xcd, 0.0));
+    std::vector<double> merged(cus_per_xcd);
     queue.assign(kPlanXcds, {});
     const int wg = std::min(wg_per_unit, cus_per_xcd);
     double end = 0.0;
     for (int i = 0; i < static_cast<int>(list.size()); ++i) {
+        const double c = list[i].cost;
         int best = 0;
         double best_end = 0.0;
         for (int x = 0; x < kPlanXcds; ++x) {
             // the unit's last workgroup starts when its wg-th compute unit frees
-            auto it = free_at[x].begin();
-            std::advance(it, wg - 1);
-            const double e = *it + list[i].cost;
+            const double e = free_at[x][wg - 1] + c;
             if (x == 0 || e < best_end || (e == best_end && queue[x].size() < queue[best].size())) {
                 best = x;
                 best_end = e;
             }
         }
-        for (int w = 0; w < wg_per_unit; ++w) {
-            const double t = *free_at[best].begin() + list[i].cost;
-            free_at[best].erase(free_at[best].begin());
-            free_at[best].insert(t);
-            end = std::max(end, t);
+        // the k compute units free first take a workgroup each: their times
+        // grow by c and merge back into the sorted rest
+        std::vector<double> &f = free_at[best];
+        for (int left = wg_per_unit; left > 0;) {
+            const int k = std::min(left, cus_per_xcd);
+            end = std::max(end, f[k - 1] + c);
+            for (int w = 0; w < k; ++w) f[w] += c;
+            std::merge(f.begin(), f.begin() + k, f.begin() + k, f.end(), merged.begin());
+            f.swap(merged);
+            left -= k;
         }
         queue[best].push_back(i);
     }
@@ -665,15 +670,36 @@ extern "C" int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_ind
         max_steps = std::max(max_steps, steps[t]);
     }
     const int cus_per_xcd = num_cus / kPlanXcds;
+    // candidate split sets: every tile above a fraction of the longest, cut
+    // in the middle, and the N longest tiles, cut at 3/10 of their steps
+    std::vector<int> by_len(num_q_tiles);
+    for (int t = 0; t < num_q_tiles; ++t) by_len[t] = t;
+    std::stable_sort(by_len.begin(), by_len.end(), [&](int a, int b) { return steps[a] > steps[b]; });
+    struct Candidate {
+        std::vector<char> split;
+        int num, den;
+    };
+    std::vector<Candidate> cands;
+    for (int k = 9; k >= 3; --k) {
+        const int64_t thr = static_cast<int64_t>(max_steps) * k / 10;
+        Candidate c{std::vector<char>(num_q_tiles, 0), 1, 2};
+        for (int t = 0; t < num_q_tiles; ++t) c.split[t] = steps[t] > thr;
+        cands.push_back(std::move(c));
+    }
+    for (int top : {1, 2, 3, 4, 5, 6, 8, 10, 12, 16}) {
+        if (top >= num_q_tiles) break;
+        Candidate c{std::vector<char>(num_q_tiles, 0), 3, 10};
+        for (int i = 0; i < top; ++i) c.split[by_len[i]] = 1;
+        cands.push_back(std::move(c));
+    }
     std::vector<std::vector<int>> queue, cand_queue;
-    std::vector<PlanUnit> best = plan_units(steps, INT32_MAX);
+    std::vector<PlanUnit> best = plan_units(steps, std::vector<char>(num_q_tiles, 0), 1, 2);
     const double base_end = deal(best, workgroups_per_tile, cus_per_xcd, queue);
     double best_end = base_end;
     std::vector<PlanUnit> chosen;
     std::vector<std::vector<int>> chosen_queue;
-    for (int k = 9; k >= 3; --k) {
-        const int thr = static_cast<int>(static_cast<int64_t>(max_steps) * k / 10);
-        std::vector<PlanUnit> cand = plan_units(steps, thr);
+    for (const Candidate &c : cands) {
+        std::vector<PlanUnit> cand = plan_units(steps, c.split, c.num, c.den);
         const double end = deal(cand, workgroups_per_tile, cus_per_xcd, cand_queue);
         if (end < best_end) {
             best_end = end;

@@ -401,11 +401,11 @@ def _plan_rule(meta, wg, num_cus):
         rows_of.append([int(rpi[b]), int(qo[b]) + row0, min(qt, e - row0), p + row0] if ok else [0, 0, 0, 0])
     big = 2 ** 31 - 1
 
-    def units(thr):
+    def units(split, num, den):
         out = []
         for t, n in enumerate(steps):
-            if n >= 2 and n > thr:
-                h = n // 2
+            if t in split and n >= 2:
+                h = max(1, n * num // den)
                 out += [(8.5 + h, t, 0, 0, h), (9.5 + n - h, t, 1, h, big)]
             else:
                 out.append((7.0 + n if n > 0 else 0.1, t, -1, 0, big))
@@ -426,11 +426,14 @@ def _plan_rule(meta, wg, num_cus):
             queue[x].append(u)
         return end, queue
 
-    base, queue = deal(units(big))
+    base, queue = deal(units(set(), 1, 2))
     mx = max(steps) if steps else 0
+    by_len = sorted(range(len(steps)), key=lambda t: -steps[t])      # stable: ties by tile order
+    cands = [({t for t, n in enumerate(steps) if n > mx * k // 10}, 1, 2) for k in range(9, 2, -1)]
+    cands += [(set(by_len[:top]), 3, 10) for top in (1, 2, 3, 4, 5, 6, 8, 10, 12, 16) if top < len(steps)]
     best_end, best_q = base, None
-    for k in range(9, 2, -1):
-        e, q = deal(units(mx * k // 10))
+    for split, num, den in cands:
+        e, q = deal(units(split, num, den))
         if e < best_end:
             best_end, best_q = e, q
     if best_q is not None and best_end <= 0.90 * base:
