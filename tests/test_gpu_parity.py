@@ -59,9 +59,9 @@ def _pre(seed, **kw):
 
 
 DECODE = {
-    "cfg1": lambda: make_case(1),
-    "cfg2": lambda: make_case(2),
-    "cfg2-seed101": lambda: make_case(2, 101),
+    "decode-contig-f32-b2": lambda: make_case(1),
+    "decode-page1-b8": lambda: make_case(2),
+    "decode-page1-b8-seed101": lambda: make_case(2, 101),
     "page16-3layers-chunk512": lambda: _dec(11, batch=12, split_chunk=512, len_hi=3000,
                                             log_uniform=True, n_layers=3, random_layer=True),
     "single-split-direct": lambda: _dec(12, batch=5, split_chunk=256, len_hi=256, page_size=1,
@@ -76,9 +76,9 @@ DECODE = {
 }
 
 PREFILL = {
-    "cfg3": lambda: make_case(3),
-    "cfg4": lambda: make_case(4),
-    "cfg4-seed101": lambda: make_case(4, 101),
+    "prefill-contig-b4": lambda: make_case(3),
+    "prefill-radix-b16": lambda: make_case(4),
+    "prefill-radix-b16-seed101": lambda: make_case(4, 101),
     "tiny-extends": lambda: _pre(21, batch=7, ext_lo=1, ext_hi=3),
     "ragged-65-129": lambda: _pre(22, batch=3, ext_lo=63, ext_hi=130),
     "prefix-page16-g1-d64": lambda: _pre(23, n_heads=4, n_kv_heads=4, head_dim=64, mode=1,
@@ -121,7 +121,7 @@ def test_rope_table_matches_oracle(d):
     assert np.all(np.abs(got - want) <= ulp)
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg3", "cfg2", "g6-d64", "prefix-f32-d64", "cfg4"])
+@pytest.mark.parametrize("name", ["decode-contig-f32-b2", "prefill-contig-b4", "decode-page1-b8", "g6-d64", "prefix-f32-d64", "prefill-radix-b16"])
 def test_rope_kv_write(name):
     cs = (DECODE.get(name) or PREFILL.get(name))()
     say(f"rope_kv_write case={name} seed={cs.seed} tokens={cs.n_new}")
@@ -220,7 +220,7 @@ def test_decode_parity(name):
         E.assert_close(got[b], want[b], cs.dtype, f"{name} request {b} (L={cs.seq_lens[b]})")
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg2", "g2-d128-f32", "g8-d128"])
+@pytest.mark.parametrize("name", ["decode-contig-f32-b2", "decode-page1-b8", "g2-d128-f32", "g8-d128"])
 def test_decode_work_items_equal_full_grid(name):
     """The work-item grid (one workgroup per split that holds keys) gives the
     same bits as the full (entry, split) grid, also with the items listed in
@@ -246,7 +246,7 @@ def test_decode_work_items_equal_full_grid(name):
         E.assert_close(got[b], want[b], cs.dtype, f"{name} request {b}")
 
 
-FUSED = [n for n in DECODE if n not in ("cfg1", "g2-d128-f32", "g4-d64-f32-page1")]   # bf16, one new token each
+FUSED = [n for n in DECODE if n not in ("decode-contig-f32-b2", "g2-d128-f32", "g4-d64-f32-page1")]   # bf16, one new token each
 
 
 @pytest.mark.parametrize("name", FUSED)
@@ -383,7 +383,7 @@ def _corrupt_table(st, cs, rng, per_request=6):
     return key_ok
 
 
-@pytest.mark.parametrize("name", ["cfg4", "ragged-65-129", "tiny-extends", "prefix-g8-d128",
+@pytest.mark.parametrize("name", ["prefill-radix-b16", "ragged-65-129", "tiny-extends", "prefix-g8-d128",
                                   "prefix-g6-d64", "prefix-page16-g1-d64", "prefix-f32-d64"])
 def test_prefill_keys_outside_pool_take_no_part(name):
     cs = PREFILL[name]()
@@ -400,7 +400,7 @@ def test_prefill_keys_outside_pool_take_no_part(name):
         E.assert_close(got[off[b]:off[b + 1]], want[b], cs.dtype, f"{name} request {b}")
 
 
-@pytest.mark.parametrize("name", ["cfg2", "g8-d128", "g6-d64", "g2-d128-f32", "length-one-and-two"])
+@pytest.mark.parametrize("name", ["decode-page1-b8", "g8-d128", "g6-d64", "g2-d128-f32", "length-one-and-two"])
 def test_decode_keys_outside_pool_take_no_part(name):
     cs = DECODE[name]()
     say(f"decode with table entries outside the pool, case={name} seed={cs.seed}")
@@ -415,7 +415,7 @@ def test_decode_keys_outside_pool_take_no_part(name):
         E.assert_close(got[b], want[b], cs.dtype, f"{name} request {b}")
 
 
-@pytest.mark.parametrize("name", ["cfg4", "prefix-g6-d64", "prefix-f32-d64"])
+@pytest.mark.parametrize("name", ["prefill-radix-b16", "prefix-g6-d64", "prefix-f32-d64"])
 def test_last_prefill_row_equals_decode(name):
     cs = PREFILL[name]()
     say(f"prefill last row vs decode, case={name}")
@@ -495,7 +495,7 @@ def _with_plan(cache, units, pairs, n_heads, workspace=None):
                                prefill_workspace=workspace), workspace
 
 
-@pytest.mark.parametrize("name", ["cfg4", "ragged-65-129", "tiny-extends", "prefix-g8-d128",
+@pytest.mark.parametrize("name", ["prefill-radix-b16", "ragged-65-129", "tiny-extends", "prefix-g8-d128",
                                   "wide-slot-g4-kv64-d128"])
 def test_prefill_forced_split_matches_oracle(name):
     cs = PREFILL[name]()
@@ -527,7 +527,7 @@ def test_prefill_forced_split_matches_oracle(name):
         assert int(counts.abs().sum()) == 0, "completion counts must be zero after a call"
 
 
-@pytest.mark.parametrize("name", ["cfg4", "cfg4-seed101", "cfg3", "prefix-g8-d128"])
+@pytest.mark.parametrize("name", ["prefill-radix-b16", "prefill-radix-b16-seed101", "prefill-contig-b4", "prefix-g8-d128"])
 def test_prefill_plan_matches_unplanned(name):
     cs = PREFILL[name]()
     st = staging.stage(cs)
