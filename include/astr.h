@@ -287,9 +287,10 @@ int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, 
  *         (q_tile must be 64), and the optional work plan (prefill_units,
  *         num_prefill_units, num_prefill_pairs, prefill_workspace)
  * sm_scale <= 0 means 1/sqrt(head_dim).  A plan changes the order of the
- * softmax sums, not the result beyond rounding.  Errors: INVAL (also: a plan
- * without workspace, a workspace smaller than its plan needs, units not
- * 16-byte aligned, more units than 16 * num_q_tiles), UNSUPPORTED, LAUNCH.
+ * softmax sums, not the result beyond rounding.  Errors: INVAL (also: split
+ * tiles without a workspace, more split tiles than half the units, a
+ * workspace smaller than its plan needs, units not 16-byte aligned, more
+ * units than 16 * num_q_tiles), UNSUPPORTED, LAUNCH.
  */
 int astr_prefill_attn(const void *q, void *out, int total_q, int n_heads,
                       const astr_kv_meta *m, int layer_id, float sm_scale, void *stream);

@@ -266,6 +266,9 @@ extern "C" int astr_prefill_attn(const void *q, void *out, int total_q, int n_he
     if (m->prefill_units || m->num_prefill_units || m->num_prefill_pairs) {
         if (!m->prefill_units || m->num_prefill_units < 1 || m->num_prefill_pairs < 0)
             return fail(ASTR_E_INVAL, "prefill_attn: incomplete work plan");
+        if (m->num_prefill_pairs > m->num_prefill_units / 2)
+            return fail(ASTR_E_INVAL, "prefill_attn: %d split tiles need %d units, the plan has %d",
+                        m->num_prefill_pairs, 2 * m->num_prefill_pairs, m->num_prefill_units);
         if (reinterpret_cast<uintptr_t>(m->prefill_units) % 16 != 0)
             return fail(ASTR_E_INVAL, "prefill_attn: work plan units not 16-byte aligned");
         if (m->num_prefill_pairs > 0 && !m->prefill_workspace)

@@ -542,6 +542,8 @@ def test_prefill_plan_errors_and_abi_checks():
     assert call() == L.ASTR_E_INVAL and b"incomplete" in so.astr_last_error()
     m.num_prefill_units, m.prefill_units = 6, 0x8004     # misaligned
     assert call() == L.ASTR_E_INVAL and b"aligned" in so.astr_last_error()
+    m.prefill_units, m.num_prefill_pairs = 0x8000, 4     # more pairs than units can hold
+    assert call() == L.ASTR_E_INVAL and b"split tiles" in so.astr_last_error()
     m.prefill_units, m.num_prefill_pairs = 0x8000, 1     # pairs without workspace
     assert call() == L.ASTR_E_INVAL and b"workspace" in so.astr_last_error()
     m.prefill_workspace = 0x9000
