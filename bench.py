@@ -56,7 +56,7 @@ KERNEL_SOURCES = {"decode": "paged_gqa_attention_rope_amd/csrc/decode.hip",
                   "prefill": "paged_gqa_attention_rope_amd/csrc/prefill.hip"}
 # kernels (name prefixes in the rocprofv3 counter CSV) that make up each call
 CALL_KERNELS = {"decode": ("decode_mfma_kernel<128, 4, false>", "decode_merge_kernel<astr::bf16_t, 128>"),
-                "prefill": ("prefill_pp_kernel<4, false>",)}
+                "prefill": ("prefill_rs_kernel<4, false>",)}
 
 
 def _sha(path: str) -> str:

@@ -84,10 +84,10 @@ struct PrefillArgs {
 
 // Prefill workspace of a plan: per (pair, KV head, group of 4 query heads) a
 // completion count, then two partial results of kPrefillPartFloats floats:
-// O^T accumulators [8 waves][2 heads][8 column blocks][4][64 lanes] and
-// (max, sum) [8 waves][2 heads][2][64 lanes] (lanes innermost, so that one
-// store or load of a wave covers 256 contiguous bytes).
-constexpr int64_t kPrefillPartFloats = 8 * 2 * 8 * 64 * 4 + 8 * 2 * 64 * 2;
+// O^T accumulators [4 row blocks][4 heads][8 column blocks][64 lanes][4] and
+// (max, sum) [4 row blocks][4 heads][2][64 lanes] (one 16-byte store per lane,
+// a wave's covering 1 KB).
+constexpr int64_t kPrefillPartFloats = 4 * 4 * 8 * 64 * 4 + 4 * 4 * 2 * 64;
 inline int64_t prefill_part_slots(int64_t pairs, int n_heads) { return pairs * ((n_heads + 3) / 4); }
 inline int64_t prefill_counts_bytes(int64_t slots) { return (4 * slots + 255) / 256 * 256; }
 

@@ -8,9 +8,14 @@
 // Causal Masking": position i attends keys j <= i; with a cached prefix of
 // p = L - e positions, query i of the request sits at position p + i.
 //
-// Two kernels:
-//  * prefill_mfma (bf16): one workgroup per (query tile, KV head, pair of query
-//    heads); its 4 waves hold 16 rows x 2 heads each.  Keys stream through a
+// Three kernels:
+//  * prefill_rs (bf16, head_dim 128, a multiple of 4 query heads per KV head;
+//    the one that follows a prefill work plan): 8 waves per (query tile or
+//    plan unit, KV head, 4 query heads), split into score waves and output
+//    waves (see the kernel).
+//  * prefill_mfma (bf16, the other head counts and head_dim 64): one
+//    workgroup per (query tile, KV head, pair of query heads); its 4 waves
+//    hold 16 rows x 2 heads each.  Keys stream through a
 //    4-deep LDS ring in steps of 32, filled by asynchronous global->LDS copies
 //    issued 3 steps ahead (slot indices 5 steps ahead), so no register
 //    staging and no wait for memory in the loop.  QK^T and PV run on the
@@ -721,48 +726,6 @@ __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kern
     }
 }
 
-// ---------------------------------------------------------------------------
-// ping-pong kernel: D = 128, a multiple of 4 query heads per KV head
-// ---------------------------------------------------------------------------
-// On gfx950 a wave's matrix-core products and its vector ALU work do not
-// overlap, but those of two waves sharing a SIMD do, provided one is in its
-// matrix-core phase while the other is in its vector phase (measured: a
-// product stream next to an ALU stream of half its length costs about as much
-// as the product stream alone; two waves running the same mixed stream in
-// step cost more than the two run one after the other).  So one workgroup of
-// 8 waves takes a query tile and 4 query heads of a KV head: waves 0-3
-// (group A) hold heads 0-1 and waves 4-7 (group B) heads 2-3 of the same 64
-// rows, and the hardware places waves w and w+4 on one SIMD.  Every wave
-// alternates
-//   VALU(s): LDS reads of K(s+1); mask, running max and P(s) =
-//            exp2(S(s)); slot indices and row copies for later steps;
-//   MFMA(s): LDS reads of V(s) (they land while the next products run);
-//            S(s+1) = K(s+1) Q^T and O^T += V(s)^T P(s)^T (+ row sums);
-// and group B runs one phase behind group A, with a workgroup barrier at the
-// end of every phase: while A multiplies, B forms probabilities, and the
-// other way round.  Keys arrive through a ring of 6 LDS slots by
-// asynchronous copies issued 4 steps ahead (slot indices 6 steps ahead), so
-// copies have at least 5 phases to land; all waits are explicit counts.
-// Step t's slot is read from K(t)'s read in VALU(t-1) (group A) to V(t)'s in
-// MFMA(t) (group B), i.e. phases 2t-1 .. 2t+3; step t+6 is copied into it
-// from VALU(t+2) on, phase 2t+5 or later.
-// The vector phase is kept short:
-//  * Q is multiplied by scale*log2(e) and rounded to bf16 once, when it is
-//    loaded, and every score accumulator starts at -m (the running max), so
-//    the products deliver the exponent itself and P needs only the exp2 and
-//    the bf16 packing.  The extra rounding of Q adds a relative error of at
-//    most 2^-9 per element of q; on the radix-prefix batch the relative L2
-//    error against the float64 definition goes from 2.4e-3 to 2.9e-3.
-//  * The keys of a step whose slot lies outside the pool are found by one
-//    ballot over the step's 32 slot indices, read from the index ring a
-//    phase ahead; no per-wave flags are written.
-//  * The raise test of the running max is one ballot per head.
-// Measured against prefill_mfma_kernel: about 15% faster on 64 requests of
-// 2048 cached + 64 new tokens, about 5% on 16 requests with radix prefixes,
-// whose time is set by the longest tile (one workgroup per CU).  Moving the
-// maxima or the probabilities into the matrix-core phase, or reading V there
-// in the vector phase instead, was measured slower or level.
-
 // Keep a value's computation before this point: an empty asm that reads and
 // rewrites the registers (volatile asm statements keep their order, and the
 // phase barriers are volatile asm).
@@ -774,17 +737,53 @@ __device__ __forceinline__ void pin(T (&x)[N]) {
     for (int i = 0; i < N; ++i) pin(x[i]);
 }
 
-struct PpCfg {
-    static constexpr int D = 128, TQ = 64, HW = 2, WAVES = 8, THREADS = 64 * WAVES;
+// ---------------------------------------------------------------------------
+// role-split kernel: D = 128, a multiple of 4 query heads per KV head
+// ---------------------------------------------------------------------------
+// One workgroup of 8 waves per (query tile or plan unit, KV head, 4 query
+// heads).  Waves 0-3 are score waves: wave w holds rows 16w .. 16w+15 of the
+// tile for all 4 heads, forms S(t) = K(t) Q^T on the matrix cores, masks it,
+// keeps the running max and writes P(t) = exp2(S(t) - m) (bf16, in the
+// matrix-core operand layout) to an LDS ring.  Waves 4-7 are output waves:
+// wave 4+w holds the O^T accumulators of the same rows and heads and, one
+// step later, reads P(t) and V(t) and adds O^T += V^T P^T (and the row sums
+// against a ones operand).  Waves w and w+4 share a SIMD, so one runs mostly
+// products and the other the vector work of the softmax; the score waves
+// raise their priority while they issue their products, so that those go
+// first and the output waves' products fill the matrix core while the score
+// waves form P.  Each K and V operand is read from LDS once per wave that
+// needs it (four times per step each).  One barrier per step: in iteration t
+// the score waves form P(t) while the output waves consume P(t-1).  A raise
+// of the running max travels with P (a flag and the per-row factors), and
+// the output waves rescale before adding.
+// Keys arrive through a ring of 6 LDS slots by asynchronous copies issued 4
+// steps ahead by all 8 waves (slot indices 6 steps ahead); every wait is an
+// explicit count.  Steps are numbered from the unit's first step t0; ring
+// slot and P slot follow t - t0.
+// Q is multiplied by scale*log2(e) and rounded to bf16 once, when it is
+// loaded, and every score accumulator starts at -m (the running max), so the
+// products deliver the exponent itself and P needs only the exp2 and the
+// bf16 packing (the extra rounding of Q adds a relative error of at most 2^-9
+// per element of q; on the radix-prefix batch the relative L2 error against
+// the float64 definition goes from 2.4e-3 to 2.9e-3).  The keys of a step
+// whose slot lies outside the pool are found by one ballot over its 32 slot
+// indices, and the raise test of the running max is one ballot per head.
+// Measured against an earlier design of this kernel, where two groups of 4
+// waves alternated product and vector phases with a barrier per phase: 3-6%
+// faster on 16 requests with radix prefixes, ~2% on 64 requests of 2048
+// cached + 64 new tokens, same error.
+struct RsCfg {
+    static constexpr int D = 128, TQ = 64, HW = 4, WAVES = 8, THREADS = 64 * WAVES;
     static constexpr int TS = 32, NB = 6, NI = 8;     // keys per step, ring slots, index slots
     static constexpr int KS = D / 32, DB = D / 16, SL = D / 8, RB = 2 * D, MAT = TS * RB;
     static constexpr int SLOT = 2 * MAT;               // one step's K rows, then its V rows
     static constexpr int RPI = 1024 / RB;              // rows one wave-wide 16-byte copy fills
+    static constexpr int PSLOT = 4 * HW * 64 * 16;     // one step's P of the 4 score waves
     static_assert(RPI * WAVES == TS, "one K and one V copy per wave and step");
 };
 
 template <int G, bool WIDE>
-__global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
+__global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
     const uint16_t *__restrict__ q, uint16_t *__restrict__ out, const uint16_t *__restrict__ k_layer,
     const uint16_t *__restrict__ v_layer, int64_t pool_slots, int n_kv,
     const int32_t *__restrict__ req_to_token, int num_reqs, int max_ctx_len,
@@ -793,10 +792,10 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     const int32_t *__restrict__ q_tile_to_index, int batch, int total_q, int n_heads,
     int num_q_tiles, float scale_log2, const int32_t *__restrict__ units, int num_units, int num_pairs,
     int32_t *__restrict__ part_cnt, float *__restrict__ part) {
-    using C = PpCfg;
+    using C = RsCfg;
     constexpr int D = C::D, TQ = C::TQ, HW = C::HW, KS = C::KS, DB = C::DB, SL = C::SL, RB = C::RB;
     constexpr int MAT = C::MAT, SLOT = C::SLOT, TS = C::TS, NB = C::NB, NI = C::NI, RPI = C::RPI;
-    constexpr int WAVES = C::WAVES;
+    constexpr int WAVES = C::WAVES, PSLOT = C::PSLOT;
     constexpr int GROUPS = G / 4;                      // workgroups per KV head
     constexpr float kLazy = 8.f;
     static_assert(G % 4 == 0, "4 query heads per workgroup");
@@ -839,10 +838,11 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp_b = __builtin_amdgcn_readfirstlane(wave >= 4 ? 1 : 0);   // group B: one phase behind
+    const int outw = __builtin_amdgcn_readfirstlane(wave >= 4 ? 1 : 0);   // output wave
     const int g = lane >> 4, j = lane & 15;
-    const int r0 = 16 * (wave & 3);                    // first tile row of this wave
-    const int h0 = kvh * G + 4 * hg + 2 * (wave >> 2); // first query head of this wave
+    const int rb = wave & 3;                           // row block of this wave
+    const int r0 = 16 * rb;
+    const int h0 = kvh * G + 4 * hg;                   // first of the 4 query heads
     const int qpos0 = ti.p + ti.row0 + r0;
     const int qpos = qpos0 + j;
     // this unit's key steps [t0, t1), and the keys its copies may fetch
@@ -851,65 +851,18 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     const int kv_lim = min(ti.kv_end, TS * t1);
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NB * SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t pring[2 * PSLOT];   // P of steps t - t0 = 0, 1 mod 2
+    __shared__ float alpha_s[2][4][HW][16];            // per P slot, row block, head, row
+    __shared__ uint32_t aflag[2][4];                   // a raise of the max in that step
+    __shared__ int32_t sidx[NI][WAVES][RPI];           // slot indices of a step's rows
+    __shared__ float m_s[4][HW][16];                   // running max handed to the output waves
+    __shared__ int32_t seen;                           // a split half's completion count
     auto slot_ptr = [&](auto rc) -> uint8_t * {
         constexpr int R = decltype(rc)::value;
         return ring + R * SLOT;
     };
-    __shared__ int32_t sidx[NI][WAVES][RPI];          // slot indices of a step's rows
 
-    Frag8 qf[HW][KS];
-    {
-        int r = r0 + j;
-        if (r >= ti.rows) r = 0;
-        const uint16_t *src = q + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h0) * D + 8 * g;
-#pragma unroll
-        for (int hh = 0; hh < HW; ++hh) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                Frag8 raw;
-                raw.u = *reinterpret_cast<const uint4 *>(src + hh * D + 32 * ks);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float lo = __uint_as_float(raw.w[e] << 16) * scale_log2;
-                    const float hi = __uint_as_float(raw.w[e] & 0xffff0000u) * scale_log2;
-                    qf[hh][ks].w[e] = cvt_pk_bf16(lo, hi);
-                }
-            }
-        }
-    }
-    f32x4_t o[HW][DB], osum[HW];
-    // m: running row max (log2 domain); bias = -m (0 while nothing is
-    // visible) starts each score accumulator, so a product's result is
-    // already the exponent; thr: accumulator value above which m is raised
-    float m[HW], neg_m[HW], thr[HW];
-    f32x4_t bias[HW];
-#pragma unroll
-    for (int hh = 0; hh < HW; ++hh) {
-        m[hh] = -INFINITY;
-        neg_m[hh] = 0.f;
-        thr[hh] = -INFINITY;
-        bias[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        osum[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[hh][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    Frag8 ones;
-    ones.u = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
-    pin(ones);                                         // a register, not rematerialised each step
-
-    uint32_t kofs[KS], vofs[DB];
-    {
-        const uint32_t kb0 = RB * j + 16 * (g ^ swz<D>(j));
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kofs[ks] = kb0 ^ (64 * ks);
-        const int vr = 4 * g + (j >> 2);
-        const uint32_t vb0 = RB * vr + 8 * (j & 1) + 16 * (((j & 3) >> 1) ^ swz<D>(vr));
-#pragma unroll
-        for (int db = 0; db < DB; ++db) vofs[db] = vb0 ^ (32 * db);
-    }
-
-    // copies: wave w fills rows 4w .. 4w+3 of a step (lane l: row 4w + l/16,
-    // chunk position l % 16, reading chunk (l % 16) ^ swz(row))
+    // ---- copies (all waves): wave w fills rows 4w .. 4w+3 of a step ----
     const int crow = RPI * wave + lane / SL;
     const uint32_t ccol = (WIDE ? 0 : kvh * RB) + 16 * ((lane % SL) ^ swz<D>(crow));
     const int32_t *trow = req_to_token + static_cast<int64_t>(ti.req) * max_ctx_len;
@@ -923,7 +876,6 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     const i32x4_t trs = buffer_rsrc(trow, 0, 4u * static_cast<uint32_t>(ti.kv_end));
     const uint32_t idx_voff = 4u * (RPI * wave + lane);
     const uint32_t sidx_base = lds_addr(sidx) + 4u * RPI * wave;
-
     // slot indices of step t's rows 4w .. 4w+3 into index slot t % NI
     auto fetch_idx = [&](int t) {
         const uint32_t soff = __builtin_amdgcn_readfirstlane(4u * TS * t);
@@ -936,7 +888,6 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
     // rows of step t into ring slot R (t >= t1, or past the visible keys:
     // out-of-range records, which read zeros; the copy count never changes)
     auto issue = [&](auto rc, int t, int32_t sl) {
-        constexpr int R = decltype(rc)::value;
         const bool ok = static_cast<uint32_t>(sl) < slot_lim;
         uint32_t rec;
         if constexpr (WIDE) rec = ok ? static_cast<uint32_t>(sl) * n_kv + kvh : 0xffffffffu;
@@ -946,148 +897,30 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         copy_record16_to_lds(krs, rec, ccol, dk);
         copy_record16_to_lds(vrs, rec, ccol, dk + MAT);
     };
-    // bit k: key k of step t has its slot in the pool.  The 32 slot indices
-    // of a step lie contiguously in its index slot (wave w's 4 rows at 4w);
-    // every wave's index copy of step t landed (and was waited for) before it
-    // issued its rows of t, several barriers ago.
+    // bit k: key k of step t has its slot in the pool (the 32 slot indices of
+    // a step lie contiguously in its index slot; every wave's index copy of
+    // step t landed before it issued its rows of t, several barriers ago)
     auto idx_of_step = [&](int t) -> int32_t { return (&sidx[t & (NI - 1)][0][0])[lane & 31]; };
     auto ok_bits = [&](int32_t ix) -> uint32_t {
         return static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(static_cast<uint32_t>(ix) < slot_lim));
     };
-    auto load_k = [&](auto rc, Frag8 (&kf)[KS][2]) {
-        const uint8_t *base = slot_ptr(rc);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                kf[ks][kb].u = *reinterpret_cast<const uint4 *>(base + 16 * RB * kb + kofs[ks]);
-        }
-    };
-    auto load_v = [&](auto rc, Frag8 (&vf)[DB]) {
-        const uint8_t *vbase = slot_ptr(rc) + MAT;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            vf[db].h[0] = lds_read_tr16(reinterpret_cast<const uint16_t *>(vbase + vofs[db]));
-            vf[db].h[1] = lds_read_tr16(reinterpret_cast<const uint16_t *>(vbase + 16 * RB + vofs[db]));
-        }
-    };
-    auto qk = [&](const Frag8 (&kf)[KS][2], f32x4_t (&sc)[HW][2]) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int hh = 0; hh < HW; ++hh)
-                    sc[hh][kb] = mfma16(kf[ks][kb], qf[hh][ks], ks == 0 ? bias[hh] : sc[hh][kb]);
-            }
-        }
-    };
-    auto probs = [&](const f32x4_t (&sc)[HW][2], Frag8 (&pf)[HW]) {
-#pragma unroll
-        for (int hh = 0; hh < HW; ++hh) {
-            float p[2][4];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) p[kb][r] = __builtin_amdgcn_exp2f(sc[hh][kb][r]);
-            }
-            pf[hh].w[0] = cvt_pk_bf16(p[0][0], p[0][1]);
-            pf[hh].w[1] = cvt_pk_bf16(p[0][2], p[0][3]);
-            pf[hh].w[2] = cvt_pk_bf16(p[1][0], p[1][1]);
-            pf[hh].w[3] = cvt_pk_bf16(p[1][2], p[1][3]);
-        }
-    };
-    auto pv = [&](const Frag8 (&vf)[DB], const Frag8 (&pf)[HW]) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-            for (int hh = 0; hh < HW; ++hh) o[hh][db] = mfma16(vf[db], pf[hh], o[hh][db]);
-        }
-#pragma unroll
-        for (int hh = 0; hh < HW; ++hh) osum[hh] = mfma16(ones, pf[hh], osum[hh]);
-    };
-    auto local_max = [&](const f32x4_t (&sc)[HW][2], float (&lm)[HW]) {
-#pragma unroll
-        for (int hh = 0; hh < HW; ++hh)
-            lm[hh] = fmaxf(fmaxf(fmaxf(sc[hh][0][0], sc[hh][0][1]), fmaxf(sc[hh][0][2], sc[hh][0][3])),
-                           fmaxf(fmaxf(sc[hh][1][0], sc[hh][1][1]), fmaxf(sc[hh][1][2], sc[hh][1][3])));
-    };
-    auto apply_mask = [&](f32x4_t (&sc)[HW][2], int kb0, uint32_t okw) __attribute__((always_inline)) {
-#pragma unroll
-        for (int hh = 0; hh < HW; ++hh) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int k = 16 * kb + 4 * g + r;
-                    if (!((okw >> k) & 1u) || kb0 + k > qpos) sc[hh][kb][r] = -INFINITY;
-                }
-            }
-        }
-    };
-    // Raise the running max where a score exceeds it by more than kLazy (as
-    // in prefill_mfma_kernel); returns whether the accumulators must be
-    // rescaled by alpha.  The caller rescales at once, on this rare path (it
-    // waits for the last products of the accumulators), so that no branch
-    // remains in the matrix-core phase.
-    auto update_max = [&](const float (&lm)[HW], float (&alpha)[HW], f32x4_t (&sc)[HW][2]) -> bool {
-        uint64_t fire = 0;
-#pragma unroll
-        for (int hh = 0; hh < HW; ++hh) fire |= __builtin_amdgcn_ballot_w64(lm[hh] > thr[hh]);
-        if (__builtin_expect(fire == 0, 1)) return false;
-#pragma unroll
-        for (int hh = 0; hh < HW; ++hh) {
-            const float mx = max_over_groups(lm[hh]) - neg_m[hh];       // the row max, log2 domain
-            const float mnew = mx > m[hh] + kLazy ? mx : m[hh];
-            alpha[hh] = exp2_sub(m[hh], mnew);
-            m[hh] = mnew;
-            const float nb = mnew == -INFINITY ? 0.f : -mnew;
-            const float shift = nb - neg_m[hh];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) sc[hh][kb] += shift;
-            neg_m[hh] = nb;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {                // in place: no copies on the common path
-                float x = bias[hh][r];
-                asm volatile("v_mov_b32 %0, %1" : "+v"(x) : "v"(nb));
-                bias[hh][r] = x;
-            }
-            thr[hh] = mnew == -INFINITY ? -INFINITY : kLazy;
-        }
-        return true;
-    };
-    auto rescale = [&](const float (&alpha)[HW]) {
-#pragma unroll
-        for (int hh = 0; hh < HW; ++hh) {
-            osum[hh] *= alpha[hh];
-#pragma unroll
-            for (int db = 0; db < DB; ++db) o[hh][db] *= alpha[hh];
-        }
-    };
-    // keys of a step whose slot lies in the pool, from its per-wave bytes
-    // d0, d1 (bit 4w + r <- wave w's bit r)
-    // a phase ends: this wave's LDS traffic is complete, then all waves meet;
+    // a step ends: this wave's LDS traffic is complete, then all waves meet;
     // no instruction moves across it
     auto phase_end = [&]() {
         __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
-    // Copy bookkeeping: each VALU(s) issues 3 copies, the indices of step
-    // s+6 then the K and V rows of step s+4.  Step t's rows must land by the
-    // end of phase 2t-2 (K(t) is first read in phase 2t-1), which falls in
-    // MFMA(t-2) for group A and in VALU(t-2) for group B.  Every wave waits
-    // for them at the end of its VALU(t-2), when 6 copies have been issued
-    // after them (for group A one phase earlier than needed, which costs
-    // nothing measurable and keeps every wait a constant count).
-    // Steps are numbered from the unit's first, t0 (0 for a whole tile); the
-    // ring slot of step t is (t - t0) % NB.  A unit with no steps (a plan's
-    // upper half past a short tile's end) keeps the empty state.
-    if (t0 < t1) {
-        // prologue: indices of steps t0..t0+5, rows of steps t0..t0+3, in the
-        // order that puts exactly 6 copies after the rows of step t0+2 by the
-        // end of VALU(t0), as in every later step (each index copy waited for
-        // by the count of copies issued after it)
+    // this lane's 16-byte P slice of head hh in P slot P
+    auto p_addr = [&](auto pc, int hh) -> uint8_t * {
+        constexpr int P = decltype(pc)::value;
+        return pring + P * PSLOT + ((rb * HW + hh) * 64 + lane) * 16;
+    };
+    // prologue: indices of steps t0..t0+5, rows of steps t0..t0+3, in the
+    // order that leaves exactly 8 copies after the rows of step t0+1 at the
+    // end of the first iteration (as after the rows of step t+1 at the end of
+    // iteration t); each index copy is waited for by the count issued after it
+    auto prologue = [&]() {
         for (int t = t0; t < t0 + 5; ++t) fetch_idx(t);
         wait_copies<4>();
         issue(int_c<0>{}, t0, slot_index(t0));
@@ -1100,79 +933,268 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         issue(int_c<3>{}, t0 + 3, slot_index(t0 + 3));
         wait_copies<7>();                              // rows of step t0
         phase_end();
-        if (grp_b) {                                   // B: idle first phase
-            wait_copies<5>();                          // rows of step t0+1
-            phase_end();
-        }
-        f32x4_t sc[HW][2];
-        {
-            Frag8 kf[KS][2];
-            load_k(int_c<0>{}, kf);
-            __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0)
-            qk(kf, sc);
-            pin(sc);
-        }
-        if (!grp_b) wait_copies<5>();                  // A: rows of step t0+1
-        phase_end();
+    };
 
-        // keys of step t0 with a slot in the pool (its indices landed in the prologue)
+    // Every iteration t (t0 .. t1, one barrier each): both roles first take
+    // the slot index of step t+4 (its copy landed: 5 copies were issued after
+    // it); after their work, the indices of step t+6 and the rows of step t+4,
+    // then the wait for the rows of step t+1 (8 copies were issued after them).
+    // The two roles run apart (their barriers meet: every wave of the
+    // workgroup passes the same number of them in the same order).
+    constexpr int64_t kPart = kPrefillPartFloats;
+    constexpr int kML = 4 * HW * DB * 4 * 64;          // offset of (m, l) in a workspace part
+    static_assert(kML + 4 * HW * 64 * 2 == kPart, "workspace layout");
+    const int64_t ps = (static_cast<int64_t>(pw < 0 ? 0 : pw >> 1) * n_kv + kvh) * GROUPS + hg;   // part slot
+    if (!outw) {
+        // ================= score waves =================
+        float m[HW];                                   // running row max (log2 domain)
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) m[hh] = -INFINITY;
+        if (t0 < t1) {
+        Frag8 qf[HW][KS];
+        {
+            int r = r0 + j;
+            if (r >= ti.rows) r = 0;
+            const uint16_t *src = q + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h0) * D + 8 * g;
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    Frag8 raw;
+                    raw.u = *reinterpret_cast<const uint4 *>(src + hh * D + 32 * ks);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float lo = __uint_as_float(raw.w[e] << 16) * scale_log2;
+                        const float hi = __uint_as_float(raw.w[e] & 0xffff0000u) * scale_log2;
+                        qf[hh][ks].w[e] = cvt_pk_bf16(lo, hi);
+                    }
+                }
+            }
+        }
+        // bias = -m (0 while nothing is visible) starts each score
+        // accumulator, so a product's result is already the exponent; thr:
+        // accumulator value above which m is raised
+        float neg_m[HW], thr[HW];
+        f32x4_t bias[HW];
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+            neg_m[hh] = 0.f;
+            thr[hh] = -INFINITY;
+            bias[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        uint32_t kofs[KS];
+        {
+            const uint32_t kb0 = RB * j + 16 * (g ^ swz<D>(j));
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kofs[ks] = kb0 ^ (64 * ks);
+        }
+        prologue();
         uint32_t okw_cur = ok_bits(idx_of_step(t0));
         // first step whose keys cross the causal diagonal of this wave's first row
         const int s_diag = (qpos0 + 1) / TS;
-        // one step: VALU(s), then MFMA(s); true after the last one
-        auto step = [&](auto rc, int s) -> bool {
+        auto step = [&](auto rc, int t) -> bool {
             constexpr int R = decltype(rc)::value;
-            constexpr int R1 = (R + 1) % NB, R4 = (R + 4) % NB;
-            const bool more = s + 1 < t1;
-            // the small LDS reads first (LDS reads complete in order, so nothing
-            // below waits for the K operands): the slot indices of step s+4, whose
-            // copy has landed (5 copies were issued after it), and the 32 slot
-            // indices of step s+1; then the K operands of step s+1
+            constexpr int R4 = (R + 4) % NB;
+            constexpr int P = R & 1;
             wait_copies<5>();
-            const int32_t sl4 = slot_index(s + 4);
-            // step s+1's keys with a slot in the pool, as a scalar mask for
-            // VALU(s+1), so that no phase waits for the read
-            const int32_t nix = idx_of_step(s + 1);
-            const uint32_t okw = okw_cur;
-            // (K is read unconditionally, so that the compiler's count of
-            // outstanding LDS reads stays exact; after the last step it goes unused)
-            Frag8 kf[KS][2], vf[DB], pf[HW];
-            load_k(int_c<R1>{}, kf);
-            {
-                float lm[HW], alpha[HW];
-                if (__builtin_expect(s >= s_diag || okw != 0xffffffffu, 0)) apply_mask(sc, TS * s, okw);
-                local_max(sc, lm);
-                if (__builtin_expect(update_max(lm, alpha, sc), 0)) rescale(alpha);
+            const int32_t sl4 = slot_index(t + 4);
+            const int32_t nix = idx_of_step(t + 1);
+            if (t < t1) {
+                Frag8 kf[KS][2];
+                const uint8_t *base = slot_ptr(rc);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+                        kf[ks][kb].u = *reinterpret_cast<const uint4 *>(base + 16 * RB * kb + kofs[ks]);
+                }
+                f32x4_t sc[HW][2];
+                __builtin_amdgcn_s_setprio(3);         // the products of S(t) go first
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                        for (int hh = 0; hh < HW; ++hh)
+                            sc[hh][kb] = mfma16(kf[ks][kb], qf[hh][ks], ks == 0 ? bias[hh] : sc[hh][kb]);
+                    }
+                }
+                __builtin_amdgcn_s_setprio(0);
+                const uint32_t okw = okw_cur;
+                if (__builtin_expect(t >= s_diag || okw != 0xffffffffu, 0)) {
+                    const int kb0 = TS * t;
+#pragma unroll
+                    for (int hh = 0; hh < HW; ++hh) {
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int k = 16 * kb + 4 * g + r;
+                                if (!((okw >> k) & 1u) || kb0 + k > qpos) sc[hh][kb][r] = -INFINITY;
+                            }
+                        }
+                    }
+                }
+                float lm[HW];
+                uint64_t fire = 0;
+#pragma unroll
+                for (int hh = 0; hh < HW; ++hh) {
+                    lm[hh] = fmaxf(fmaxf(fmaxf(sc[hh][0][0], sc[hh][0][1]), fmaxf(sc[hh][0][2], sc[hh][0][3])),
+                                   fmaxf(fmaxf(sc[hh][1][0], sc[hh][1][1]), fmaxf(sc[hh][1][2], sc[hh][1][3])));
+                    fire |= __builtin_amdgcn_ballot_w64(lm[hh] > thr[hh]);
+                }
+                uint32_t flag = 0;
+                if (__builtin_expect(fire != 0, 0)) {
+                    // Raise the running max where a score exceeds it by more than
+                    // kLazy (exact: the same stale max enters numerator and
+                    // denominator, and probabilities stay below 2^8), and hand the
+                    // factors to the output wave of these rows.
+#pragma unroll
+                    for (int hh = 0; hh < HW; ++hh) {
+                        const float mx = max_over_groups(lm[hh]) - neg_m[hh];   // the row max
+                        const float mnew = mx > m[hh] + kLazy ? mx : m[hh];
+                        const float alpha = exp2_sub(m[hh], mnew);
+                        m[hh] = mnew;
+                        const float nb = mnew == -INFINITY ? 0.f : -mnew;
+                        const float shift = nb - neg_m[hh];
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) sc[hh][kb] += shift;
+                        neg_m[hh] = nb;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {          // in place: no copies on the common path
+                            float x = bias[hh][r];
+                            asm volatile("v_mov_b32 %0, %1" : "+v"(x) : "v"(nb));
+                            bias[hh][r] = x;
+                        }
+                        thr[hh] = mnew == -INFINITY ? -INFINITY : kLazy;
+                        if (g == 0) alpha_s[P][rb][hh][j] = alpha;
+                    }
+                    flag = 1;
+                }
+                if (lane == 0) aflag[P][rb] = flag;
+#pragma unroll
+                for (int hh = 0; hh < HW; ++hh) {
+                    float p[2][4];
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) p[kb][r] = __builtin_amdgcn_exp2f(sc[hh][kb][r]);
+                    }
+                    uint4 w;
+                    w.x = cvt_pk_bf16(p[0][0], p[0][1]);
+                    w.y = cvt_pk_bf16(p[0][2], p[0][3]);
+                    w.z = cvt_pk_bf16(p[1][0], p[1][1]);
+                    w.w = cvt_pk_bf16(p[1][2], p[1][3]);
+                    *reinterpret_cast<uint4 *>(p_addr(int_c<P>{}, hh)) = w;
+                }
             }
-            probs(sc, pf);
-            pin(pf);                                   // P(s) is formed in this phase
-            fetch_idx(s + 6);
-            issue(int_c<R4>{}, s + 4, sl4);
+            fetch_idx(t + 6);
+            issue(int_c<R4>{}, t + 4, sl4);
             okw_cur = ok_bits(nix);
-            // rows of step s+2 (6 copies were issued after them): group B reads
-            // K(s+2) in its next phase; group A only after its MFMA(s)
-            wait_copies<6>();
+            wait_copies<8>();
             phase_end();
-            load_v(rc, vf);
-            if (more) {
-                qk(kf, sc);
-                pin(sc);                               // S(s+1) is formed in this phase
-            }
-            pv(vf, pf);
-            pin(o);
-            pin(osum);
-            phase_end();
-            return !more;
+            return t >= t1;
         };
-        for (int s = t0;; s += NB) {
-            if (step(int_c<0>{}, s)) break;
-            if (step(int_c<1>{}, s + 1)) break;
-            if (step(int_c<2>{}, s + 2)) break;
-            if (step(int_c<3>{}, s + 3)) break;
-            if (step(int_c<4>{}, s + 4)) break;
-            if (step(int_c<5>{}, s + 5)) break;
+        for (int t = t0;; t += NB) {
+            if (step(int_c<0>{}, t)) break;
+            if (step(int_c<1>{}, t + 1)) break;
+            if (step(int_c<2>{}, t + 2)) break;
+            if (step(int_c<3>{}, t + 3)) break;
+            if (step(int_c<4>{}, t + 4)) break;
+            if (step(int_c<5>{}, t + 5)) break;
         }
-        if (!grp_b) phase_end();                       // A: idle last phase
+        wait_copies<0>();
+        }
+        if (pw < 0) return;
+        // a split half: hand the running max to the output waves, then take
+        // part in the publish / merge barriers (tid 0 keeps the count)
+        int32_t *cnt = part_cnt + ps;
+        if (g == 0) {
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) m_s[rb][hh][j] = m[hh];
+        }
+        if (tid == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (seen == 0) {
+            __syncthreads();                           // the output waves' stores are complete
+            if (tid == 0) seen = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (seen == 0) return;                     // the other half merges
+        }
+        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // for the next call
+        return;
+    }
+    // ================= output waves =================
+    f32x4_t o[HW][DB], osum[HW];
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+        osum[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[hh][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if (t0 < t1) {
+        Frag8 ones;
+        ones.u = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+        pin(ones);                                     // a register, not rematerialised each step
+        uint32_t vofs[DB];
+        {
+            const int vr = 4 * g + (j >> 2);
+            const uint32_t vb0 = RB * vr + 8 * (j & 1) + 16 * (((j & 3) >> 1) ^ swz<D>(vr));
+#pragma unroll
+            for (int db = 0; db < DB; ++db) vofs[db] = vb0 ^ (32 * db);
+        }
+        prologue();
+        auto step = [&](auto rc, int t) -> bool {
+            constexpr int R = decltype(rc)::value;
+            constexpr int R4 = (R + 4) % NB, RP = (R + NB - 1) % NB;   // ring slot of step t-1
+            constexpr int P = (R + 1) & 1;                           // P slot of step t-1
+            wait_copies<5>();
+            const int32_t sl4 = slot_index(t + 4);
+            if (t > t0) {
+                // P(t-1) and V(t-1) (written / landed before the last barrier)
+                const uint32_t fl = aflag[P][rb];
+                Frag8 pf[HW], vf[DB];
+#pragma unroll
+                for (int hh = 0; hh < HW; ++hh) pf[hh].u = *reinterpret_cast<const uint4 *>(p_addr(int_c<P>{}, hh));
+                const uint8_t *vbase = slot_ptr(int_c<RP>{}) + MAT;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    vf[db].h[0] = lds_read_tr16(reinterpret_cast<const uint16_t *>(vbase + vofs[db]));
+                    vf[db].h[1] = lds_read_tr16(reinterpret_cast<const uint16_t *>(vbase + 16 * RB + vofs[db]));
+                }
+                if (__builtin_expect(__builtin_amdgcn_readfirstlane(static_cast<int>(fl)) != 0, 0)) {
+#pragma unroll
+                    for (int hh = 0; hh < HW; ++hh) {
+                        const float a = alpha_s[P][rb][hh][j];
+                        osum[hh] *= a;
+#pragma unroll
+                        for (int db = 0; db < DB; ++db) o[hh][db] *= a;
+                    }
+                }
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                    for (int hh = 0; hh < HW; ++hh) o[hh][db] = mfma16(vf[db], pf[hh], o[hh][db]);
+                }
+#pragma unroll
+                for (int hh = 0; hh < HW; ++hh) osum[hh] = mfma16(ones, pf[hh], osum[hh]);
+                pin(o);
+                pin(osum);
+            }
+            fetch_idx(t + 6);
+            issue(int_c<R4>{}, t + 4, sl4);
+            wait_copies<8>();
+            phase_end();
+            return t >= t1;
+        };
+        for (int t = t0;; t += NB) {
+            if (step(int_c<0>{}, t)) break;
+            if (step(int_c<1>{}, t + 1)) break;
+            if (step(int_c<2>{}, t + 2)) break;
+            if (step(int_c<3>{}, t + 3)) break;
+            if (step(int_c<4>{}, t + 4)) break;
+            if (step(int_c<5>{}, t + 5)) break;
+        }
         wait_copies<0>();
     }
 
@@ -1187,43 +1209,45 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
         // count (vector memory counter at zero), and read back with
         // agent-coherent loads issued after the count was seen, so the halves
         // may run on any two XCDs; no wave ever waits for another workgroup.
-        constexpr int64_t kPart = kPrefillPartFloats;
-        constexpr int kML = WAVES * HW * DB * 64 * 4;    // offset of (m, l) in a part
-        static_assert(kML + WAVES * HW * 64 * 2 == kPart, "workspace layout");
-        const int64_t ps = (static_cast<int64_t>(pw >> 1) * n_kv + kvh) * GROUPS + hg;
-        int32_t *cnt = part_cnt + ps;
-        float *mine = part + (2 * ps + (pw & 1)) * kPart;
-        const float *other = part + (2 * ps + ((pw & 1) ^ 1)) * kPart;
-        __shared__ int32_t seen;
-        // has the other half already published its state?
-        if (tid == 0) seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
+        // agent-coherent (sc1) buffer stores and loads over the two parts; a
+        // part holds the O^T accumulators as [row block][head][column block]
+        // [lane][4] (one 16-byte store per lane, a wave's covering 1 KB), then
+        // (max, sum) as [row block][head][2][lane]
+        constexpr uint32_t kAgent = 16;                // cache policy: scope bit sc1
+        using u32x4_t = __attribute__((ext_vector_type(4))) unsigned int;
+        const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+            part + (2 * ps + (pw & 1)) * kPart, 0, static_cast<int>(4 * kPart), 0x00020000);
+        const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
+            part + (2 * ps + ((pw & 1) ^ 1)) * kPart, 0, static_cast<int>(4 * kPart), 0x00020000);
+        __syncthreads();                               // the running max and the count are in LDS
+        float m[HW];
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) m[hh] = m_s[rb][hh][j];
         if (seen == 0) {
 #pragma unroll
             for (int hh = 0; hh < HW; ++hh) {
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
+                    u32x4_t v;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        __hip_atomic_store(mine + (((wave * HW + hh) * DB + db) * 4 + e) * 64 + lane, o[hh][db][e],
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(o[hh][db][e]);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, mr, 16 * (((rb * HW + hh) * DB + db) * 64 + lane), 0,
+                                                           kAgent);
                 }
-                float *ml = mine + kML + (wave * HW + hh) * 128 + lane;
-                __hip_atomic_store(ml, m[hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(ml + 64, osum[hh][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int ml = 4 * (kML + (rb * HW + hh) * 128 + lane);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m[hh]), mr, ml, 0, kAgent);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(osum[hh][0]), mr, ml + 256, 0, kAgent);
             }
             __builtin_amdgcn_s_waitcnt(0);             // every store of this wave is complete
             __syncthreads();                           // ... and of every wave
-            if (tid == 0) seen = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
+            __syncthreads();                           // the count is in LDS
             if (seen == 0) return;                     // the other half merges
         }
-        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // for the next call
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
-            const float *ml = other + kML + (wave * HW + hh) * 128 + lane;
-            const float mo = __hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float lo = __hip_atomic_load(ml + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int ml = 4 * (kML + (rb * HW + hh) * 128 + lane);
+            const float mo = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orr, ml, 0, kAgent));
+            const float lo = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orr, ml + 256, 0, kAgent));
             const float mx = fmaxf(m[hh], mo);
             const float a = mx == -INFINITY ? 0.f : exp2_sub(m[hh], mx);
             const float b = mx == -INFINITY ? 0.f : exp2_sub(mo, mx);
@@ -1231,31 +1255,46 @@ __global__ __launch_bounds__(PpCfg::THREADS, 1) void prefill_pp_kernel(
             osum[hh] = f32x4_t{l, l, l, l};
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
+                const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
+                    orr, 16 * (((rb * HW + hh) * DB + db) * 64 + lane), 0, kAgent);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x = __hip_atomic_load(other + (((wave * HW + hh) * DB + db) * 4 + e) * 64 + lane,
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    o[hh][db][e] = o[hh][db][e] * a + x * b;
-                }
+                for (int e = 0; e < 4; ++e) o[hh][db][e] = o[hh][db][e] * a + __uint_as_float(x[e]) * b;
             }
+            __builtin_amdgcn_sched_barrier(0);         // one head's loads in flight at a time
         }
     }
 
     const int r = r0 + j;
+    if (r < ti.rows) {
 #pragma unroll
-    for (int hh = 0; hh < HW; ++hh) {
-        const float ls = osum[hh][0];
-        if (r >= ti.rows) continue;
-        const float inv = ls > 0.f ? 1.f / ls : 0.f;
-        uint16_t *dst = out + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h0 + hh) * D + 4 * g;
+        for (int hh = 0; hh < HW; ++hh) {
+            const float ls = osum[hh][0];
+            const float inv = ls > 0.f ? 1.f / ls : 0.f;
+            uint16_t *dst = out + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h0 + hh) * D + 4 * g;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            uint2 w;
-            w.x = cvt_pk_bf16(o[hh][db][0] * inv, o[hh][db][1] * inv);
-            w.y = cvt_pk_bf16(o[hh][db][2] * inv, o[hh][db][3] * inv);
-            *reinterpret_cast<uint2 *>(dst + 16 * db) = w;
+            for (int db = 0; db < DB; ++db) {
+                uint2 w;
+                w.x = cvt_pk_bf16(o[hh][db][0] * inv, o[hh][db][1] * inv);
+                w.y = cvt_pk_bf16(o[hh][db][2] * inv, o[hh][db][3] * inv);
+                *reinterpret_cast<uint2 *>(dst + 16 * db) = w;
+            }
         }
     }
+}
+
+template <int G, bool WIDE>
+hipError_t launch_rs(const PrefillArgs &a, hipStream_t s) {
+    const int n = a.num_units > 0 ? a.num_units : a.num_q_tiles;
+    const int64_t units = static_cast<int64_t>((n + kXcds - 1) / kXcds) * kXcds * a.pool.n_kv_heads * (G / 4);
+    hipLaunchKernelGGL((prefill_rs_kernel<G, WIDE>), dim3(static_cast<unsigned>(units)), dim3(RsCfg::THREADS),
+                       0, s, static_cast<const uint16_t *>(a.q), static_cast<uint16_t *>(a.out),
+                       static_cast<const uint16_t *>(a.pool.k_layer),
+                       static_cast<const uint16_t *>(a.pool.v_layer), a.pool.pool_slots,
+                       a.pool.n_kv_heads, a.req_to_token, a.num_reqs, a.max_ctx_len, a.req_pool_indices,
+                       a.qo_indptr, a.kv_indptr, a.q_tile_to_batch, a.q_tile_to_index, a.batch,
+                       a.total_q, a.n_heads, a.num_q_tiles, a.scale_log2, a.units, a.num_units, a.num_pairs,
+                       a.part_cnt, a.part);
+    return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -1284,27 +1323,12 @@ hipError_t launch_mfma(const PrefillArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int G, bool WIDE>
-hipError_t launch_pp(const PrefillArgs &a, hipStream_t s) {
-    const int n = a.num_units > 0 ? a.num_units : a.num_q_tiles;
-    const int64_t units = static_cast<int64_t>((n + kXcds - 1) / kXcds) * kXcds * a.pool.n_kv_heads * (G / 4);
-    hipLaunchKernelGGL((prefill_pp_kernel<G, WIDE>), dim3(static_cast<unsigned>(units)), dim3(PpCfg::THREADS),
-                       0, s, static_cast<const uint16_t *>(a.q), static_cast<uint16_t *>(a.out),
-                       static_cast<const uint16_t *>(a.pool.k_layer),
-                       static_cast<const uint16_t *>(a.pool.v_layer), a.pool.pool_slots,
-                       a.pool.n_kv_heads, a.req_to_token, a.num_reqs, a.max_ctx_len, a.req_pool_indices,
-                       a.qo_indptr, a.kv_indptr, a.q_tile_to_batch, a.q_tile_to_index, a.batch,
-                       a.total_q, a.n_heads, a.num_q_tiles, a.scale_log2, a.units, a.num_units, a.num_pairs,
-                       a.part_cnt, a.part);
-    return hipGetLastError();
-}
-
 template <int D, bool WIDE>
 hipError_t launch_mfma_g(const PrefillArgs &a, hipStream_t s) {
     if constexpr (D == 128) {
         switch (a.n_heads / a.pool.n_kv_heads) {
-            case 4: return launch_pp<4, WIDE>(a, s);
-            case 8: return launch_pp<8, WIDE>(a, s);
+            case 4: return launch_rs<4, WIDE>(a, s);
+            case 8: return launch_rs<8, WIDE>(a, s);
             default: break;
         }
     }
