@@ -72,8 +72,9 @@ __device__ __forceinline__ bool tile_info(int t, const int32_t *q_tile_to_batch,
     ti.p = ti.L - ti.e;
     ti.row0 = idx * q_tile;
     if (idx < 0 || ti.e <= 0 || ti.p < 0 || ti.row0 >= ti.e) return false;
-    if (ti.q0 < 0 || ti.q0 > total_q - ti.e) return false;
     ti.rows = min(q_tile, ti.e - ti.row0);
+    // the tile's rows must lie in [0, total_q)
+    if (ti.q0 < 0 || static_cast<int64_t>(ti.q0) + ti.row0 + ti.rows > total_q) return false;
     ti.kv_end = ti.p + ti.row0 + ti.rows;       // keys seen by the tile's last row
     return true;
 }

@@ -548,3 +548,31 @@ def test_prefill_plan_matches_unplanned(name):
         E.assert_close(b_[off[b]:off[b + 1]], want[b], cs.dtype, f"{name} unplanned request {b}")
     # the two differ only in the order of the softmax sums
     assert np.linalg.norm(a - b_) <= 2e-3 * np.linalg.norm(b_)
+
+
+@pytest.mark.parametrize("plan", [False, True])
+def test_prefill_tiles_past_total_q_are_skipped(plan):
+    # q and out hold fewer rows than qo_indptr asks for: a tile whose rows
+    # fall outside [0, total_q) is skipped (its rows stay as they were), every
+    # other tile is computed as usual
+    cs = PREFILL["ragged-65-129"]()
+    off = E.new_offsets(cs)
+    b = next(i for i in range(cs.batch) if cs.new_lens[i] >= 75)
+    cut = int(off[b]) + 64 + 5                   # request b keeps its first tile, loses the rest
+    say(f"prefill with total_q {cut} of {int(off[-1])} rows, plan={plan}")
+    st = staging.stage(cs, plan=plan)
+    staging.run_write(st)
+    q = st.q[:cut].contiguous()
+    out = torch.full_like(q, float("nan"))
+    astr.prefill_attn(q, st.attn_cache, cs.layer_id, out=out)
+    torch.cuda.synchronize()
+    want = E.expected_prefill(cs)
+    got = to_np(out)
+    for r in range(cs.batch):
+        for t in range(-(-int(cs.new_lens[r]) // 64)):
+            lo, hi = int(off[r]) + 64 * t, min(int(off[r]) + 64 * (t + 1), int(off[r + 1]))
+            if hi <= cut:
+                E.assert_close(got[lo:hi], want[r][lo - int(off[r]):hi - int(off[r])], cs.dtype,
+                               f"request {r} tile {t}")
+            elif lo < cut:
+                assert np.isnan(got[lo:cut]).all(), f"request {r} tile {t} crosses total_q and must be skipped"
