@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
     constexpr int KS = D / 32;          // k-steps of S^T
     constexpr int DB = D / 16;          // 16-row blocks of O^T
     constexpr int CK = 32;              // keys per wave chunk
-    constexpr int LDV = D + 8;          // padded LDS row, bf16 elements
+    constexpr int RB = 2 * D;           // LDS row bytes (unpadded; chunks XOR-swizzled)
     constexpr int WAVES = 4;
     static_assert(G <= 16, "query heads per KV head must fit the 16 MFMA columns");
 
@@ -293,12 +293,12 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
 
     // LDS: one tile per wave (the chunk's K rows, then its V rows), then the
     // cross-wave merge
-    constexpr int T_BYTES = WAVES * CK * LDV * 2;
+    constexpr int T_BYTES = WAVES * CK * RB;
     constexpr int M_BYTES = WAVES * G * (D + 2) * 4;
     constexpr int S_BYTES = T_BYTES > M_BYTES ? T_BYTES : M_BYTES;
     constexpr int N_BYTES = FUSED ? 4 * D : 0;     // the new token's rotated k and v rows
     __shared__ __attribute__((aligned(16))) char smem[S_BYTES + N_BYTES];
-    uint16_t *sT = reinterpret_cast<uint16_t *>(smem) + wave * CK * LDV;
+    char *sT = smem + wave * CK * RB;
     uint16_t *s_new = reinterpret_cast<uint16_t *>(smem + S_BYTES);
 
     Frag8 qf[KS];
@@ -359,6 +359,10 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
             *reinterpret_cast<uint4 *>(v_store + off) = nv;
         }
     }
+    // tile byte offsets this lane writes: row i*RPI + rr, chunk cc
+    int wofs[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) wofs[i] = RB * (i * RPI + rr) + 16 * (cc ^ swz<D>(i * RPI + rr));
     int32_t sl_now = slot_of(start + wave * CK);
     for (int c0 = start + wave * CK; c0 < end; c0 += WAVES * CK) {
         const int32_t sl_next = slot_of(c0 + WAVES * CK);
@@ -378,25 +382,26 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
         // the chunk holding the new token: its row of the LDS tile takes the
         // rotated k_new / v_new staged above
         const bool mine = has_new && c0 <= npos && npos < c0 + CK;
+        const int nofs = RB * (npos - c0) + 16 * (cc ^ swz<D>(npos - c0));
         // bit k: key c0 + k exists and has a valid slot
         const uint32_t okmask = static_cast<uint32_t>(
             __ballot(c0 + (lane & 31) < end && sl_now >= 0 && sl_now < pool_slots) & 0xffffffffull);
         // K rows -> LDS -> MFMA A-operand layout (lane: key 16kb + j, d = 32ks + 8g)
 #pragma unroll
-        for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4 *>(sT + (i * RPI + rr) * LDV + 8 * cc) = kx[i];
-        if (mine) *reinterpret_cast<uint4 *>(sT + (npos - c0) * LDV + 8 * cc) = *reinterpret_cast<const uint4 *>(s_new + 8 * cc);
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4 *>(sT + wofs[i]) = kx[i];
+        if (mine) *reinterpret_cast<uint4 *>(sT + nofs) = *reinterpret_cast<const uint4 *>(s_new + 8 * cc);
         wave_lds_fence();
         Frag8 kf[2][KS];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kf[kb][ks].u = *reinterpret_cast<const uint4 *>(sT + (16 * kb + j) * LDV + 32 * ks + 8 * g);
+                kf[kb][ks].u = *reinterpret_cast<const uint4 *>(sT + RB * (16 * kb + j) + 16 * ((4 * ks + g) ^ swz<D>(j)));
         }
         wave_lds_fence();                       // K read out before V overwrites the tile
 #pragma unroll
-        for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4 *>(sT + (i * RPI + rr) * LDV + 8 * cc) = vx[i];
-        if (mine) *reinterpret_cast<uint4 *>(sT + (npos - c0) * LDV + 8 * cc) = *reinterpret_cast<const uint4 *>(s_new + D + 8 * cc);
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4 *>(sT + wofs[i]) = vx[i];
+        if (mine) *reinterpret_cast<uint4 *>(sT + nofs) = *reinterpret_cast<const uint4 *>(s_new + D + 8 * cc);
         f32x4_t sc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -442,12 +447,15 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
         pf.w[2] = pack_bf16x2(sc[1][0], sc[1][1]);
         pf.w[3] = pack_bf16x2(sc[1][2], sc[1][3]);
         wave_lds_fence();                       // V tile written by all lanes of this wave
-        const uint16_t *va = sT + (4 * g + (j >> 2)) * LDV + 4 * (j & 3);
+        // lane (g, j): 8 bytes at byte 8(j & 3) + 32db of row 4g + j/4 (and 16 rows on)
+        const int vr = 4 * g + (j >> 2);
+        const char *va = sT + RB * vr + 8 * (j & 1);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             Frag8 vf;
-            vf.h[0] = lds_read_tr16(va + 16 * db);
-            vf.h[1] = lds_read_tr16(va + 16 * LDV + 16 * db);
+            const int vc = 16 * ((((j & 3) >> 1) + 2 * db) ^ swz<D>(vr));
+            vf.h[0] = lds_read_tr16(reinterpret_cast<const uint16_t *>(va + vc));
+            vf.h[1] = lds_read_tr16(reinterpret_cast<const uint16_t *>(va + 16 * RB + vc));
             o[db] = mfma16(vf, pf, o[db]);
         }
         wave_lds_fence();                       // reads done before the next chunk's writes

@@ -68,4 +68,19 @@ __device__ __forceinline__ void wave_lds_fence() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// LDS position of 16-byte chunk c of row r of a tile of K or V head rows
+// (unpadded, 2*D bytes each): c ^ swz(r).  The XOR swizzle keeps both the
+// 128-bit K-operand reads (16 rows, one chunk each) and the transposing V
+// reads (4 rows x 32 bytes per 16 lanes) free of LDS bank conflicts (measured
+// with the bank-conflict counter), and whole-row writes stay contiguous.
+template <int D>
+__device__ __forceinline__ constexpr int swz(int r) {
+    if constexpr (D == 128) {
+        r &= 15;
+        return ((r >> 1) ^ (r << 2)) & 15;
+    } else {
+        return r & 7;
+    }
+}
+
 }  // namespace astr

@@ -210,21 +210,6 @@ struct MfmaCfg {
     static_assert(G % HW == 0 && IPW >= 1 && TS % (RPI * WAVES) == 0, "tiling");
 };
 
-// LDS position of 16-byte chunk c of row r of a step's K or V rows: c ^ swz(r).
-// Rows are unpadded (one wave-wide asynchronous copy fills whole rows); the
-// XOR swizzle keeps both the 128-bit K-operand reads (16 rows, one chunk
-// each) and the transposing V reads (4 rows x 32 bytes per 16 lanes) free of
-// LDS bank conflicts (measured with the bank-conflict counter).
-template <int D>
-__device__ __forceinline__ constexpr int swz(int r) {
-    if constexpr (D == 128) {
-        r &= 15;
-        return ((r >> 1) ^ (r << 2)) & 15;
-    } else {
-        return r & 7;
-    }
-}
-
 // s_waitcnt immediate: at most n vector-memory operations outstanding, the
 // other counters unconstrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
