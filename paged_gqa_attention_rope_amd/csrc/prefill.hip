@@ -259,10 +259,13 @@ __device__ __forceinline__ void copy_record16_to_lds(i32x4_t rsrc, uint32_t idx,
                  "s"(rsrc), "s"(lds)
                  : "memory", "m0");
 }
-// 4 bytes at byte voff + soff of the raw buffer `rsrc`; bytes past its size read zeros.
-__device__ __forceinline__ void copy_raw4_to_lds(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
-                 "s"(soff), "s"(lds)
+// 4 bytes at byte voff of the raw buffer `rsrc`; bytes at or past its size
+// read zeros and touch no memory.  The whole offset goes in the VGPR offset:
+// the hardware range check of a raw buffer covers the VGPR and instruction
+// offsets only, not the SGPR offset.
+__device__ __forceinline__ void copy_raw4_to_lds(i32x4_t rsrc, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+                 "s"(lds)
                  : "memory", "m0");
 }
 
@@ -428,14 +431,12 @@ __global__ __launch_bounds__((MfmaCfg<D, G>::THREADS), 2) void prefill_mfma_kern
         else if constexpr (R == 2) return sidx2[wave];
         else return sidx3[wave];
     };
-    // the request's table row up to its last visible key; entries past it read 0
+    // the request's table row up to its last visible key; entries past it
+    // (steps fetched ahead of the last one) read 0 without touching memory
     const i32x4_t trs = buffer_rsrc(trow, 0, 4u * static_cast<uint32_t>(ti.kv_end));
     const uint32_t idx_voff = 4u * (8 * wave + lane);
     auto fetch_idx = [&](auto rc, int t) {
-        // the step offset as a wave-uniform register (the offset field takes no literal)
-        const uint32_t soff = __builtin_amdgcn_readfirstlane(4u * TS * t);
-        asm volatile("" : : "s"(soff));
-        if (lane < 8) copy_raw4_to_lds(trs, idx_voff, soff, lds_addr(sidx(rc)));
+        if (lane < 8) copy_raw4_to_lds(trs, idx_voff + 4u * TS * t, lds_addr(sidx(rc)));
     };
     // A key whose slot lies outside the pool, and every key of a step
     // t >= nsteps (whose rows are never used; copying zeros keeps the number
@@ -864,10 +865,8 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
     const uint32_t sidx_base = lds_addr(sidx) + 4u * RPI * wave;
     // slot indices of step t's rows 4w .. 4w+3 into index slot t % NI
     auto fetch_idx = [&](int t) {
-        const uint32_t soff = __builtin_amdgcn_readfirstlane(4u * TS * t);
-        asm volatile("" : : "s"(soff));
         const uint32_t dst = __builtin_amdgcn_readfirstlane(sidx_base + 4u * RPI * WAVES * (t & (NI - 1)));
-        if (lane < RPI) copy_raw4_to_lds(trs, idx_voff, soff, dst);
+        if (lane < RPI) copy_raw4_to_lds(trs, idx_voff + 4u * TS * t, dst);
     };
     // this lane's row's slot index of step t (its index copy has landed)
     auto slot_index = [&](int t) -> int32_t { return sidx[t & (NI - 1)][wave][lane / SL]; };
