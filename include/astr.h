@@ -33,8 +33,11 @@
  *     with the batch and sequence axes flattened, internals.md "Attention
  *     Backend"); query head h reads KV head h / (n_heads / n_kv_heads).
  *   - Supported: kv_dtype in {ASTR_F32, ASTR_BF16}; head_dim in {64, 128};
- *     n_heads / n_kv_heads in {1, 2, 4, 6, 8}.  Activations (q, out) use
- *     the pool's dtype; accumulation is float32.
+ *     n_heads / n_kv_heads in {1, 2, 4, 6, 8} (one compiled kernel per
+ *     group size; any other divisor returns ASTR_E_UNSUPPORTED).  The
+ *     device calls take the activations' dtype (act_dtype: q, k, v, out);
+ *     it must equal the pool's kv_dtype, else ASTR_E_UNSUPPORTED.
+ *     Accumulation is float32.
  */
 #ifndef ASTR_H
 #define ASTR_H
@@ -150,13 +153,14 @@ int astr_rope_table(float *freqs_cis, int max_pos, int head_dim, double theta, v
  *   freqs_cis      device [max_pos, head_dim/2, 2] float32 (astr_rope_table)
  *   m              host; uses k_buffer, v_buffer, pool_slots, n_layers,
  *                  n_kv_heads, head_dim, kv_dtype
+ *   act_dtype      dtype of q, k and v; must equal m->kv_dtype
  * n_tokens == 0 is a no-op.  Tokens whose slot or position is out of range are
  * skipped entirely.  Errors: INVAL, UNSUPPORTED, LAUNCH.
  */
 int astr_rope_kv_write(void *q, const void *k, const void *v,
                        const int32_t *positions, const int32_t *out_cache_loc,
                        int n_tokens, int n_heads, const float *freqs_cis, int max_pos,
-                       const astr_kv_meta *m, int layer_id, void *stream);
+                       const astr_kv_meta *m, int layer_id, astr_dtype act_dtype, void *stream);
 
 /*
  * Gradient of the rotation (the backward pass of the rotary embedding used in
@@ -184,6 +188,22 @@ int astr_rope_backward(void *grad, const int32_t *positions, int n_tokens, int n
 
 /* Number of KV splits S = ceil(max_len / split_chunk) (0 on bad input). */
 int astr_decode_num_splits(int max_len, int split_chunk);
+
+/*
+ * Bytes of the split-K scratch of one decode call: the partial outputs and
+ * log-sum-exps of every (request, query head, split), the decode_o_part and
+ * decode_ml_part buffers of the KVCache record (inference.md, "KVCache
+ * System") with the split axis made explicit.  With S = ceil(max_len /
+ * split_chunk) and R = batch * n_heads * S the scratch is
+ *   o_part    float32 [batch, n_heads, S, head_dim]  (R * head_dim * 4 bytes)
+ *   lse_part  float32 [batch, n_heads, S]            (R * 4 bytes)
+ * and the value returned is their sum, so that one allocation can hold both
+ * (o_part first, lse_part at byte R * head_dim * 4, a multiple of 16).  0
+ * when S <= 1 (the decode then writes its output directly and touches no
+ * scratch) and on bad input (batch < 0, n_heads < 1, head_dim < 1,
+ * max_len < 0, split_chunk < 1).
+ */
+size_t astr_decode_workspace_bytes(int batch, int n_heads, int head_dim, int max_len, int split_chunk);
 /*
  * The decode work items of a step (host only): for each batch entry b the
  * splits s < max(1, ceil(seq_lens[b] / split_chunk)) -- every (request,
@@ -221,10 +241,12 @@ int astr_decode_split_items(const int32_t *seq_lens, int batch, int split_chunk,
  * M = max_s lse_s, o = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M).
  * When S == 1 the single pass writes `out` directly and o_part / lse_part
  * are not touched (they may then be NULL).
- *   q         device [batch, n_heads, head_dim] kv_dtype (already rotated)
- *   out       device [batch, n_heads, head_dim] kv_dtype, written
+ *   q         device [batch, n_heads, head_dim] act_dtype (already rotated)
  *   o_part    device [batch, n_heads, S, head_dim] float32 scratch
- *   lse_part  device [batch, n_heads, S] float32 scratch
+ *   lse_part  device [batch, n_heads, S] float32 scratch (together
+ *             astr_decode_workspace_bytes; owned by the caller)
+ *   out       device [batch, n_heads, head_dim] act_dtype, written
+ *   act_dtype dtype of q and out; must equal m->kv_dtype
  *   m         host; uses the pool fields, req_to_token, num_reqs, max_ctx_len,
  *             req_pool_indices, kv_indptr, batch, max_len (>= every L_b;
  *             it sizes the split axis and, without work items, the grid),
@@ -233,9 +255,9 @@ int astr_decode_split_items(const int32_t *seq_lens, int batch, int split_chunk,
  *             split_item_chunk == split_chunk are required)
  * Requests with L_b == 0 get a zero output.  Errors: INVAL, UNSUPPORTED, LAUNCH.
  */
-int astr_decode_attn(const void *q, void *out, int n_heads, const astr_kv_meta *m,
-                     int layer_id, int split_chunk, float sm_scale,
-                     float *o_part, float *lse_part, void *stream);
+int astr_decode_attn(const void *q, int n_heads, const astr_kv_meta *m, int layer_id,
+                     int split_chunk, float sm_scale, float *o_part, float *lse_part,
+                     void *out, astr_dtype act_dtype, void *stream);
 
 /*
  * The decode step with its rotary write fused in (inference.md, "Attention
@@ -252,14 +274,15 @@ int astr_decode_attn(const void *q, void *out, int n_heads, const astr_kv_meta *
  *   q            device [batch, n_heads, head_dim] bf16, unrotated
  *   k_new, v_new device [batch, m->n_kv_heads, head_dim] bf16, unrotated k
  *   freqs_cis    device [max_pos, head_dim/2, 2] float32, max_pos >= m->max_len
- *   other arguments as astr_decode_attn.
+ *   other arguments as astr_decode_attn (act_dtype also covers k_new, v_new).
  * A new-token slot outside the pool is neither written nor attended.
  * Errors: as astr_decode_attn; UNSUPPORTED for a float32 pool; INVAL for null
  * k_new/v_new/freqs_cis or max_pos < max_len.
  */
-int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, void *out, int n_heads,
+int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, int n_heads,
                            const astr_kv_meta *m, int layer_id, const float *freqs_cis, int max_pos,
-                           int split_chunk, float sm_scale, float *o_part, float *lse_part, void *stream);
+                           int split_chunk, float sm_scale, float *o_part, float *lse_part,
+                           void *out, astr_dtype act_dtype, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Prefill attention (ragged batch, causal, optional cached prefix)        */
@@ -278,9 +301,12 @@ int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, 
  * q_tile_to_batch[t] (inference.md, "KVCache System").  Keys and values are
  * read straight from the pool through req_to_token (inference.md, "Attention
  * Backend": ragged prefill addressed by qo_indptr and kv_indptr).
- *   q     device [total_q, n_heads, head_dim] kv_dtype (rotated), total_q >=
- *         qo_indptr[batch]; a tile whose rows fall outside [0, total_q) is skipped
+ *   q     device [total_q, n_heads, head_dim] act_dtype (rotated), total_q >=
+ *         qo_indptr[batch]; a tile whose rows fall outside [0, total_q) is
+ *         skipped (total_q is the row count of q, which the device-side
+ *         qo_indptr cannot give the host without a read-back)
  *   out   device, same shape and dtype, written (rows of every tile)
+ *   act_dtype  dtype of q and out; must equal m->kv_dtype
  *   m     host; uses the pool fields, req_to_token, num_reqs, max_ctx_len,
  *         req_pool_indices, kv_indptr, qo_indptr, q_tile_to_batch,
  *         q_tile_to_index, batch, max_len, num_q_tiles, q_tile
@@ -292,8 +318,8 @@ int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, 
  * workspace smaller than its plan needs, units not 16-byte aligned, more
  * units than 16 * num_q_tiles), UNSUPPORTED, LAUNCH.
  */
-int astr_prefill_attn(const void *q, void *out, int total_q, int n_heads,
-                      const astr_kv_meta *m, int layer_id, float sm_scale, void *stream);
+int astr_prefill_attn(const void *q, int total_q, int n_heads, const astr_kv_meta *m,
+                      int layer_id, float sm_scale, void *out, astr_dtype act_dtype, void *stream);
 
 /*
  * Workspace of a prefill work plan with `pairs` split tiles: per pair, KV

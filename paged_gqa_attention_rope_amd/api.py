@@ -241,7 +241,7 @@ def rope_kv_write(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: 
     m.kv_dtype = _DTYPES[kb.dtype]
     check(lib().astr_rope_kv_write(_vp(q), _vp(k), _vp(v), _vp(positions), _vp(out_cache_loc), t,
                                    int(q.shape[1]), _vp(freqs_cis), int(freqs_cis.shape[0]),
-                                   ctypes.byref(m), int(layer_id), _stream(q)))
+                                   ctypes.byref(m), int(layer_id), _DTYPES[q.dtype], _stream(q)))
     return q
 
 
@@ -265,13 +265,27 @@ def decode_num_splits(max_len: int, split_chunk: int) -> int:
     return int(lib().astr_decode_num_splits(int(max_len), int(split_chunk)))
 
 
+def decode_workspace_bytes(batch: int, n_heads: int, head_dim: int, max_len: int, split_chunk: int) -> int:
+    """Bytes of the split-K scratch (o_part then lse_part) of one decode call
+    (astr_decode_workspace_bytes); 0 when one split covers max_len."""
+    return int(lib().astr_decode_workspace_bytes(int(batch), int(n_heads), int(head_dim), int(max_len),
+                                                 int(split_chunk)))
+
+
 def decode_workspace(cache: KVCache, n_heads: int, split_chunk: int):
-    """(o_part [B, H, S, D], lse_part [B, H, S]) float32 for astr_decode_attn."""
+    """(o_part [B, H, S, D], lse_part [B, H, S]) float32 for astr_decode_attn,
+    carved from one allocation of astr_decode_workspace_bytes (None, None
+    when one split covers max_len and no scratch is used)."""
     d = int(cache.k_buffer.shape[3])
+    b = cache.batch
+    nbytes = decode_workspace_bytes(b, n_heads, d, cache.max_len, split_chunk)
+    if nbytes == 0:
+        return None, None
     s = decode_num_splits(cache.max_len, split_chunk)
-    dev = cache.k_buffer.device
-    return (torch.empty((cache.batch, n_heads, s, d), dtype=torch.float32, device=dev),
-            torch.empty((cache.batch, n_heads, s), dtype=torch.float32, device=dev))
+    rows = b * n_heads * s
+    _need(nbytes == 4 * rows * (d + 1), "decode workspace size disagrees with its layout")
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=cache.k_buffer.device)
+    return ws[:rows * d].view(b, n_heads, s, d), ws[rows * d:].view(b, n_heads, s)
 
 
 def decode_attn(q: torch.Tensor, cache: KVCache, layer_id: int, split_chunk: int,
@@ -294,10 +308,9 @@ def decode_attn(q: torch.Tensor, cache: KVCache, layer_id: int, split_chunk: int
             o_part, lse_part = decode_workspace(cache, h, split_chunk)
         _dev_tensor(o_part, "o_part", torch.float32, kb.device, b * h * s * d)
         _dev_tensor(lse_part, "lse_part", torch.float32, kb.device, b * h * s)
-    check(lib().astr_decode_attn(_vp(q), _vp(out), h, ctypes.byref(m), int(layer_id),
-                                 int(split_chunk), float(sm_scale),
+    check(lib().astr_decode_attn(_vp(q), h, ctypes.byref(m), int(layer_id), int(split_chunk), float(sm_scale),
                                  _vp(o_part) if s > 1 else None, _vp(lse_part) if s > 1 else None,
-                                 _stream(q)))
+                                 _vp(out), _DTYPES[q.dtype], _stream(q)))
     return out
 
 
@@ -328,11 +341,11 @@ def decode_attn_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
             o_part, lse_part = decode_workspace(cache, h, split_chunk)
         _dev_tensor(o_part, "o_part", torch.float32, kb.device, b * h * s * d)
         _dev_tensor(lse_part, "lse_part", torch.float32, kb.device, b * h * s)
-    check(lib().astr_decode_attn_write(_vp(q), _vp(k_new), _vp(v_new), _vp(out), h, ctypes.byref(m),
+    check(lib().astr_decode_attn_write(_vp(q), _vp(k_new), _vp(v_new), h, ctypes.byref(m),
                                        int(layer_id), _vp(freqs_cis), int(freqs_cis.shape[0]),
                                        int(split_chunk), float(sm_scale),
                                        _vp(o_part) if s > 1 else None, _vp(lse_part) if s > 1 else None,
-                                       _stream(q)))
+                                       _vp(out), _DTYPES[q.dtype], _stream(q)))
     return out
 
 
@@ -347,8 +360,8 @@ def prefill_attn(q: torch.Tensor, cache: KVCache, layer_id: int, sm_scale: float
     if out is None:
         out = torch.empty_like(q)
     _dev_tensor(out, "out", kb.dtype, kb.device, q.numel())
-    check(lib().astr_prefill_attn(_vp(q), _vp(out), int(q.shape[0]), int(q.shape[1]),
-                                  ctypes.byref(m), int(layer_id), float(sm_scale), _stream(q)))
+    check(lib().astr_prefill_attn(_vp(q), int(q.shape[0]), int(q.shape[1]), ctypes.byref(m), int(layer_id),
+                                  float(sm_scale), _vp(out), _DTYPES[q.dtype], _stream(q)))
     return out
 
 

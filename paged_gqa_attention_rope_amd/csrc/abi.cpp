@@ -62,6 +62,17 @@ int check_pool(const char *who, const astr_kv_meta *m, int n_heads, int layer_id
     return ASTR_OK;
 }
 
+// Activations (q, k, v, out) are stored in the pool's dtype: the kernels
+// read and write them with the pool's element type.
+int check_act(const char *who, const astr_kv_meta *m, int act_dtype) {
+    if (act_dtype != ASTR_F32 && act_dtype != ASTR_BF16)
+        return fail(ASTR_E_UNSUPPORTED, "%s: act_dtype %d (supported: f32, bf16)", who, act_dtype);
+    if (act_dtype != m->kv_dtype)
+        return fail(ASTR_E_UNSUPPORTED, "%s: act_dtype %d differs from kv_dtype %d (activations use the pool's dtype)",
+                    who, act_dtype, m->kv_dtype);
+    return ASTR_OK;
+}
+
 int check_table(const char *who, const astr_kv_meta *m) {
     if (m->batch < 0) return fail(ASTR_E_INVAL, "%s: batch %d", who, m->batch);
     if (m->batch == 0) return ASTR_OK;
@@ -102,9 +113,11 @@ extern "C" int astr_rope_table(float *freqs_cis, int max_pos, int head_dim, doub
 extern "C" int astr_rope_kv_write(void *q, const void *k, const void *v, const int32_t *positions,
                                   const int32_t *out_cache_loc, int n_tokens, int n_heads,
                                   const float *freqs_cis, int max_pos, const astr_kv_meta *m,
-                                  int layer_id, void *stream) {
+                                  int layer_id, astr_dtype act_dtype, void *stream) {
     astr::RopeArgs a{};
     int st = astr::check_pool("rope_kv_write", m, n_heads, layer_id, a.pool);
+    if (st) return st;
+    st = astr::check_act("rope_kv_write", m, act_dtype);
     if (st) return st;
     if (n_tokens < 0) return fail(ASTR_E_INVAL, "rope_kv_write: n_tokens %d", n_tokens);
     if (n_tokens == 0) return ASTR_OK;
@@ -145,13 +158,23 @@ extern "C" int astr_decode_num_splits(int max_len, int split_chunk) {
     return s < 1 ? 1 : s;
 }
 
+extern "C" size_t astr_decode_workspace_bytes(int batch, int n_heads, int head_dim, int max_len, int split_chunk) {
+    if (batch < 0 || n_heads < 1 || head_dim < 1 || max_len < 0 || split_chunk < 1) return 0;
+    const int s = astr_decode_num_splits(max_len, split_chunk);
+    if (s <= 1) return 0;                              // one split: the output is written directly
+    const size_t rows = static_cast<size_t>(batch) * n_heads * s;
+    return rows * static_cast<size_t>(head_dim) * 4 + rows * 4;
+}
+
 namespace {
 // Shared by the plain and the fused decode call: validation and arguments.
 int decode_args(const char *what, const void *q, void *out, int n_heads, const astr_kv_meta *m,
                 int layer_id, int split_chunk, float sm_scale, float *o_part, float *lse_part,
-                astr::DecodeArgs &a, bool &empty) {
+                int act_dtype, astr::DecodeArgs &a, bool &empty) {
     empty = false;
     int st = astr::check_pool(what, m, n_heads, layer_id, a.pool);
+    if (st) return st;
+    st = astr::check_act(what, m, act_dtype);
     if (st) return st;
     st = astr::check_table(what, m);
     if (st) return st;
@@ -196,25 +219,25 @@ int decode_args(const char *what, const void *q, void *out, int n_heads, const a
 }
 }  // namespace
 
-extern "C" int astr_decode_attn(const void *q, void *out, int n_heads, const astr_kv_meta *m,
-                                int layer_id, int split_chunk, float sm_scale, float *o_part,
-                                float *lse_part, void *stream) {
+extern "C" int astr_decode_attn(const void *q, int n_heads, const astr_kv_meta *m, int layer_id,
+                                int split_chunk, float sm_scale, float *o_part, float *lse_part, void *out,
+                                astr_dtype act_dtype, void *stream) {
     astr::DecodeArgs a{};
     bool empty;
     const int st = decode_args("decode_attn", q, out, n_heads, m, layer_id, split_chunk, sm_scale, o_part,
-                               lse_part, a, empty);
+                               lse_part, act_dtype, a, empty);
     if (st || empty) return st;
     return astr::launched("decode_attn", astr::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
-extern "C" int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, void *out,
-                                      int n_heads, const astr_kv_meta *m, int layer_id,
-                                      const float *freqs_cis, int max_pos, int split_chunk, float sm_scale,
-                                      float *o_part, float *lse_part, void *stream) {
+extern "C" int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, int n_heads,
+                                      const astr_kv_meta *m, int layer_id, const float *freqs_cis, int max_pos,
+                                      int split_chunk, float sm_scale, float *o_part, float *lse_part,
+                                      void *out, astr_dtype act_dtype, void *stream) {
     astr::DecodeArgs a{};
     bool empty;
     const int st = decode_args("decode_attn_write", q, out, n_heads, m, layer_id, split_chunk, sm_scale,
-                               o_part, lse_part, a, empty);
+                               o_part, lse_part, act_dtype, a, empty);
     if (st || empty) return st;
     if (m->kv_dtype != ASTR_BF16)
         return fail(ASTR_E_UNSUPPORTED, "decode_attn_write: bf16 only (use astr_rope_kv_write + astr_decode_attn)");
@@ -228,10 +251,12 @@ extern "C" int astr_decode_attn_write(const void *q, const void *k_new, const vo
     return astr::launched("decode_attn_write", astr::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
-extern "C" int astr_prefill_attn(const void *q, void *out, int total_q, int n_heads,
-                                 const astr_kv_meta *m, int layer_id, float sm_scale, void *stream) {
+extern "C" int astr_prefill_attn(const void *q, int total_q, int n_heads, const astr_kv_meta *m,
+                                 int layer_id, float sm_scale, void *out, astr_dtype act_dtype, void *stream) {
     astr::PrefillArgs a{};
     int st = astr::check_pool("prefill_attn", m, n_heads, layer_id, a.pool);
+    if (st) return st;
+    st = astr::check_act("prefill_attn", m, act_dtype);
     if (st) return st;
     st = astr::check_table("prefill_attn", m);
     if (st) return st;

@@ -41,10 +41,7 @@ class DecodeStep:
         self.split_chunk, self.sm_scale = int(split_chunk), float(sm_scale)
         self.out = torch.empty_like(q)
         h = int(q.shape[2])
-        if api.decode_num_splits(cache.max_len, split_chunk) > 1:
-            self.o_part, self.lse_part = api.decode_workspace(cache, h, split_chunk)
-        else:
-            self.o_part = self.lse_part = None
+        self.o_part, self.lse_part = api.decode_workspace(cache, h, split_chunk)   # (None, None): one split
         self.graph: Optional[torch.cuda.CUDAGraph] = None
 
     def run(self) -> torch.Tensor:

@@ -109,14 +109,39 @@ def test_builder_bit_exact_against_oracle(cid, seed_off):
     assert rn == ro and cn == co
     assert np.array_equal(cn, cs.prefix_lens)
     assert np.array_equal(pn.table(), po.table())
-    for key in ("req_pool_indices", "seq_lens", "out_cache_loc", "kv_indptr", "qo_indptr",
-                "q_tile_to_batch", "q_tile_to_index"):
+    for key in ("req_pool_indices", "seq_lens", "out_cache_loc", "kv_indptr", "qo_indptr"):
         assert np.array_equal(np.asarray(mn[key]), np.asarray(mo[key])), key
     assert mn["num_q_tiles"] == mo["num_q_tiles"] and mn["max_len"] == mo["max_len"]
+    # the tile -> request maps are fixed, their order is not: the same set of
+    # (batch entry, tile index) pairs, each once; the builder's own order is
+    # checked against its stated rule in test_builder_lists_tiles_heaviest_first
+    tn = list(zip(np.asarray(mn["q_tile_to_batch"]).tolist(), np.asarray(mn["q_tile_to_index"]).tolist()))
+    to = list(zip(np.asarray(mo["q_tile_to_batch"]).tolist(), np.asarray(mo["q_tile_to_index"]).tolist()))
+    assert len(set(tn)) == len(tn) and sorted(tn) == sorted(to)
     if cs.mode == 1:
         assert pn.p.free_pages() == sum(po.p.free)
         for page in range(0, cs.pool_slots // cs.page_size, max(1, cs.pool_slots // cs.page_size // 97)):
             assert pn.p.page_ref(page) == po.p.ref[page]
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+@pytest.mark.parametrize("seed_off", [0, 101, 202])
+def test_builder_lists_tiles_heaviest_first(cid, seed_off):
+    """The library's own tile order (a scheduling choice, not part of the
+    definition): by decreasing KV extent seen by the tile's last row, ties by
+    batch entry, then tile index.  Stated here as a sort over the request-
+    major tiles, independently of both builders."""
+    _lib()
+    cs = make_case(cid, None if seed_off == 0 else seed_off + cid)
+    _, _, _, mn = _flow(_Native, cs)
+    e = cs.new_lens.astype(int)
+    p = (cs.seq_lens - cs.new_lens).astype(int)
+    q_tile = cs.q_tile
+    tiles = [(b, t) for b in range(cs.batch) for t in range(-(-int(e[b]) // q_tile))]
+    extent = {(b, t): int(p[b] + min(q_tile * (t + 1), e[b])) for b, t in tiles}
+    want = sorted(tiles, key=lambda bt: (-extent[bt], bt[0], bt[1]))
+    got = list(zip(mn["q_tile_to_batch"].tolist(), mn["q_tile_to_index"].tolist()))
+    assert got == want
 
 
 def test_builder_lifecycle_matches_oracle():
@@ -158,8 +183,10 @@ def test_builder_lifecycle_matches_oracle():
             reqs = [x[0] for x in live]
             q = [int(rng.integers(0, x[2] + 1)) for x in live]
             mn, mo = pn.bind(reqs, q, 8), po.bind(reqs, q, 8)
-            for key in ("out_cache_loc", "kv_indptr", "qo_indptr", "q_tile_to_batch"):
+            for key in ("out_cache_loc", "kv_indptr", "qo_indptr"):
                 assert np.array_equal(mn[key], mo[key])
+            assert sorted(zip(mn["q_tile_to_batch"].tolist(), mn["q_tile_to_index"].tolist())) == \
+                sorted(zip(mo["q_tile_to_batch"].tolist(), mo["q_tile_to_index"].tolist()))
         assert np.array_equal(pn.table(), po.table()), step
         assert pn.p.free_pages() == sum(po.p.free)
 
@@ -279,24 +306,24 @@ def test_attention_calls_validate_before_launch():
         mm = L.KvMeta.from_buffer_copy(m)
         for k, v in change.items():
             setattr(mm, k, v)
-        st = so.astr_decode_attn(ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), 8,
-                                 ctypes.byref(mm), 0, 64, 0.0, None, None, None)
+        st = so.astr_decode_attn(ctypes.c_void_p(0x2000), 8, ctypes.byref(mm), 0, 64, 0.0, None, None,
+                                 ctypes.c_void_p(0x3000), L.ASTR_BF16, None)
         assert st == want, (change, st)
-    st = so.astr_decode_attn(None, None, 8, ctypes.byref(m), 5, 64, 0.0, None, None, None)
+    st = so.astr_decode_attn(None, 8, ctypes.byref(m), 5, 64, 0.0, None, None, None, L.ASTR_BF16, None)
     assert st == L.ASTR_E_INVAL                          # layer out of range
     # the fused decode write: table first, then its own checks
     mt = L.KvMeta.from_buffer_copy(m)
     mt.req_to_token = mt.req_pool_indices = mt.kv_indptr = 0x4000
     mt.num_reqs, mt.max_ctx_len = 1, 8
     q = ctypes.c_void_p(0x2000)
-    assert so.astr_decode_attn_write(q, q, q, q, 8, ctypes.byref(mt), 0, q, 4, 64, 0.0, None, None,
-                                     None) == L.ASTR_E_INVAL              # max_pos 4 < max_len 8
-    assert so.astr_decode_attn_write(q, None, q, q, 8, ctypes.byref(mt), 0, q, 8, 64, 0.0, None, None,
-                                     None) == L.ASTR_E_INVAL              # k_new missing
+    assert so.astr_decode_attn_write(q, q, q, 8, ctypes.byref(mt), 0, q, 4, 64, 0.0, None, None, q,
+                                     L.ASTR_BF16, None) == L.ASTR_E_INVAL   # max_pos 4 < max_len 8
+    assert so.astr_decode_attn_write(q, None, q, 8, ctypes.byref(mt), 0, q, 8, 64, 0.0, None, None, q,
+                                     L.ASTR_BF16, None) == L.ASTR_E_INVAL   # k_new missing
     mt.kv_dtype = L.ASTR_F32
-    assert so.astr_decode_attn_write(q, q, q, q, 8, ctypes.byref(mt), 0, q, 8, 64, 0.0, None, None,
-                                     None) == L.ASTR_E_UNSUPPORTED        # bf16 only
-    st = so.astr_rope_kv_write(None, None, None, None, None, 0, 8, None, 1, ctypes.byref(m), 0, None)
+    assert so.astr_decode_attn_write(q, q, q, 8, ctypes.byref(mt), 0, q, 8, 64, 0.0, None, None, q,
+                                     L.ASTR_F32, None) == L.ASTR_E_UNSUPPORTED   # bf16 only
+    st = so.astr_rope_kv_write(None, None, None, None, None, 0, 8, None, 1, ctypes.byref(m), 0, L.ASTR_BF16, None)
     assert st == L.ASTR_OK                               # zero tokens: a no-op
     st = so.astr_rope_table(None, 10, 64, 10000.0, None)
     assert st == L.ASTR_E_INVAL
@@ -310,6 +337,46 @@ def test_attention_calls_validate_before_launch():
     assert so.astr_decode_num_splits(0, 256) == 1
     assert so.astr_decode_num_splits(10, 0) == 0
     assert b"rope_backward: n_tokens -1" in so.astr_last_error()
+
+
+def test_activation_dtype_must_match_the_pool():
+    """act_dtype is checked before anything is launched: a value outside the
+    enum, or activations in another dtype than the pool, are rejected."""
+    L = _lib()
+    so = L.lib()
+    m = L.KvMeta()
+    m.k_buffer = m.v_buffer = 0x1000
+    m.pool_slots, m.n_layers, m.n_kv_heads, m.head_dim, m.kv_dtype = 64, 1, 2, 128, L.ASTR_BF16
+    m.req_to_token = m.req_pool_indices = m.kv_indptr = m.qo_indptr = 0x4000
+    m.q_tile_to_batch = m.q_tile_to_index = 0x4000
+    m.num_reqs, m.max_ctx_len, m.batch, m.max_len, m.num_q_tiles, m.q_tile = 1, 8, 1, 8, 1, 64
+    q = ctypes.c_void_p(0x2000)
+    for act, want in ((L.ASTR_F32, L.ASTR_E_UNSUPPORTED), (5, L.ASTR_E_UNSUPPORTED)):
+        assert so.astr_rope_kv_write(q, q, q, q, q, 1, 8, q, 8, ctypes.byref(m), 0, act, None) == want
+        assert b"act_dtype" in so.astr_last_error()
+        assert so.astr_decode_attn(q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, q, act, None) == want
+        assert so.astr_decode_attn_write(q, q, q, 8, ctypes.byref(m), 0, q, 8, 64, 0.0, None, None, q, act,
+                                         None) == want
+        assert so.astr_prefill_attn(q, 8, 8, ctypes.byref(m), 0, 0.0, q, act, None) == want
+        assert b"act_dtype" in so.astr_last_error()
+
+
+def test_decode_workspace_bytes():
+    """The split-K scratch: float32 o_part [B, H, S, D] then lse_part [B, H, S],
+    S = ceil(max_len / chunk); nothing when one split covers max_len."""
+    L = _lib()
+    so = L.lib()
+    import paged_gqa_attention_rope_amd as astr
+    for b, h, d, ml, c in ((256, 16, 128, 32768, 512), (8, 16, 128, 2048, 256), (2, 4, 64, 33, 16),
+                           (3, 24, 64, 1000, 7), (0, 8, 128, 4000, 256)):
+        s = -(-ml // c)
+        assert so.astr_decode_workspace_bytes(b, h, d, ml, c) == 4 * b * h * s * (d + 1)
+        assert astr.decode_workspace_bytes(b, h, d, ml, c) == 4 * b * h * s * (d + 1)
+    assert so.astr_decode_workspace_bytes(4, 8, 128, 256, 256) == 0       # one split
+    assert so.astr_decode_workspace_bytes(4, 8, 128, 0, 256) == 0
+    for bad in ((-1, 8, 128, 100, 16), (4, 0, 128, 100, 16), (4, 8, 0, 100, 16), (4, 8, 128, -1, 16),
+                (4, 8, 128, 100, 0)):
+        assert so.astr_decode_workspace_bytes(*bad) == 0
 
 
 def _items_rule(lens, chunk):
@@ -361,13 +428,13 @@ def test_decode_split_items_errors_and_abi_checks():
     q = ctypes.c_void_p(0x2000)
     m.split_item_batch = 0x5000                          # index list missing
     m.num_split_items, m.split_item_chunk = 1, 64
-    assert so.astr_decode_attn(q, q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, None) == L.ASTR_E_INVAL
+    assert so.astr_decode_attn(q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, q, L.ASTR_BF16, None) == L.ASTR_E_INVAL
     m.split_item_index = 0x6000
     m.split_item_chunk = 32                              # built for another chunk
-    assert so.astr_decode_attn(q, q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, None) == L.ASTR_E_INVAL
+    assert so.astr_decode_attn(q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, q, L.ASTR_BF16, None) == L.ASTR_E_INVAL
     assert b"split_chunk 32" in so.astr_last_error()
     m.split_item_chunk, m.num_split_items = 64, 0        # no count
-    assert so.astr_decode_attn(q, q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, None) == L.ASTR_E_INVAL
+    assert so.astr_decode_attn(q, 8, ctypes.byref(m), 0, 64, 0.0, None, None, q, L.ASTR_BF16, None) == L.ASTR_E_INVAL
 
 
 # ---------------------------------------------------------------------------
@@ -536,7 +603,7 @@ def test_prefill_plan_errors_and_abi_checks():
     q = ctypes.c_void_p(0x2000)
 
     def call():
-        return so.astr_prefill_attn(q, q, 250, 16, ctypes.byref(m), 0, 0.0, None)
+        return so.astr_prefill_attn(q, 250, 16, ctypes.byref(m), 0, 0.0, q, L.ASTR_BF16, None)
 
     m.prefill_units = 0x8000                             # no count
     assert call() == L.ASTR_E_INVAL and b"incomplete" in so.astr_last_error()
