@@ -26,8 +26,9 @@ is given; slot = physical_page * page_size + pos % page_size; unused table
 entries are -1; a lookup leaves at least one prompt token to compute, so it
 matches at most floor((n_tokens - 1) / page_size) pages; query tiles cover
 q_tile rows each, the last one of a request possibly partial, and are listed
-heaviest first (by the KV extent their last row sees; ties by request, then
-tile index -- the pages fix only the tile -> request maps, not their order);
+request-major (requests in batch order, a request's tiles in row order -- the
+pages fix only the tile -> request maps, not their order, so the library may
+list them in another order of its own);
 ``out_cache_loc`` is flat in ``qo_indptr`` order.
 
 Lifecycle (same pages: the allocator's reference counts and LRU eviction;
@@ -189,17 +190,17 @@ class PagePool:
         kv_indptr = [0]
         qo_indptr = [0]
         loc = []
-        tiles = []                     # (KV extent of the tile's last row, batch entry, index)
+        t2b, t2i = [], []
         for b, (r, L, ql) in enumerate(zip(reqs, seq, q_lens)):
             kv_indptr.append(kv_indptr[-1] + L)
             qo_indptr.append(qo_indptr[-1] + ql)
             loc.extend(int(self.table[r, p]) for p in range(L - ql, L))
+            # the request's query tiles, request-major: tile t holds rows
+            # [t * q_tile, min((t + 1) * q_tile, q_len)); the pages fix which
+            # rows a tile holds, not the order in which tiles are listed
             for t in range(-(-ql // q_tile)):
-                tiles.append((L - ql + min((t + 1) * q_tile, ql), b, t))
-        # heaviest tile first; ties keep request order, then tile order
-        tiles.sort(key=lambda x: (-x[0], x[1], x[2]))
-        t2b = [b for _, b, _ in tiles]
-        t2i = [t for _, _, t in tiles]
+                t2b.append(b)
+                t2i.append(t)
         i32 = lambda a: np.asarray(a, dtype=np.int32)
         return dict(req_pool_indices=i32(reqs), seq_lens=i32(seq),
                     out_cache_loc=i32(loc), kv_indptr=i32(kv_indptr),

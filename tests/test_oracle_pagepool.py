@@ -58,12 +58,12 @@ def test_paged_slots_and_growth():
     m = pp.bind([r0, r1], [13, 16], q_tile=8)
     assert np.array_equal(m["out_cache_loc"], np.concatenate([pp.table[r0, 20:33], pp.table[r1, :16]]))
     assert np.array_equal(m["qo_indptr"], [0, 13, 29])
-    # KV extents seen by each tile's last row: (0,0) 28, (0,1) 33, (1,0) 8, (1,1) 16
+    # request-major tiles: request 0 rows [0, 8), [8, 13); request 1 rows [0, 8), [8, 16)
     assert np.array_equal(m["q_tile_to_batch"], [0, 0, 1, 1])
-    assert np.array_equal(m["q_tile_to_index"], [1, 0, 1, 0])
+    assert np.array_equal(m["q_tile_to_index"], [0, 1, 0, 1])
 
 
-def test_tile_maps_cover_every_row_heaviest_first():
+def test_tile_maps_cover_every_row_request_major():
     rng = np.random.default_rng(1)
     q = rng.integers(1, 300, size=9)
     pre = 16 * rng.integers(0, 20, size=9)
@@ -75,12 +75,10 @@ def test_tile_maps_cover_every_row_heaviest_first():
     n = -(-q // 64)
     assert m["num_q_tiles"] == n.sum()
     pairs = list(zip(m["q_tile_to_batch"].tolist(), m["q_tile_to_index"].tolist()))
-    assert sorted(pairs) == [(b, t) for b in range(9) for t in range(n[b])]
-    ext = [int(pre[b] + min(64 * (t + 1), q[b])) for b, t in pairs]
-    assert all(ext[i] >= ext[i + 1] for i in range(len(ext) - 1))
-    for i in range(len(ext) - 1):
-        if ext[i] == ext[i + 1]:
-            assert pairs[i] < pairs[i + 1]
+    assert pairs == [(b, t) for b in range(9) for t in range(n[b])]
+    # every query row lies in exactly one tile, the last tile of a request may be partial
+    rows = [(b, i) for b, t in pairs for i in range(64 * t, min(64 * (t + 1), int(q[b])))]
+    assert sorted(rows) == [(b, i) for b in range(9) for i in range(int(q[b]))]
 
 
 def test_nomem_leaves_state_unchanged():
