@@ -12,11 +12,17 @@ The page tables are built once, before timing (they are per-step host
 metadata shared by all layers); their host cost is reported separately.
 
 value = decode KV GB/s: algorithmic bytes (every cached K/V row read once,
-its slot index, q read and output written) / the decode call's device time
-(split-K pass + merge), from HIP events recorded on the stream the kernels
-run on.  The prefill figure (TFLOP/s over unmasked (query, key) pairs) is in
-"prefill".  cpu_baseline times the float64 oracle on a bounded sample of the
-decode workload on the host cores.
+its slot index, q read and output written) / the decode call's mean device
+time over the timed steps (split-K pass + merge), from HIP events recorded
+on the stream the kernels run on; the median is reported beside it.  The
+prefill figure (TFLOP/s over unmasked (query, key) pairs) is in "prefill".
+"configs" holds the other workloads: the tiny float32 decode, the
+cache-resident 8-request decode and the 4-request contiguous prefill, each
+the median of 50 calls with warm caches and with the caches flushed (a
+512 MB write between calls).  "ceilings" holds what a plain streaming read
+and a matrix-core loop attain on the same device.  cpu_baseline times the
+float64 oracle on a bounded sample of the decode workload (and, under
+"prefill", of the prefill workload) on the host cores.
 """
 
 import argparse
@@ -117,29 +123,61 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
     print(json.dumps(out, indent=1))
 
 
+def _host_cores() -> int:
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(cs, budget_s: float = 15.0):
-    """The oracle, as it stands, on a bounded sample of the decode workload."""
+    """The oracle, as it stands, on a bounded sample of the decode workload:
+    requests in batch order until budget_s has passed, BLAS on every core
+    this process may run on."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import expect as E
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
+    cores = _host_cores()
     rot = E.rotated_new(cs)
-    t0 = time.perf_counter()
     done, nbytes = [], 0
     esz = 2
-    for b in range(cs.batch):
-        E.expected_decode(cs, sample=[b], rot=rot)
-        done.append(b)
-        nbytes += int(cs.seq_lens[b]) * (cs.n_kv_heads * cs.head_dim * esz * 2 + 4) + \
-            cs.n_heads * cs.head_dim * esz * 2
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    with threadpool_limits(cores):
+        t0 = time.perf_counter()
+        for b in range(cs.batch):
+            E.expected_decode(cs, sample=[b], rot=rot)
+            done.append(b)
+            nbytes += int(cs.seq_lens[b]) * (cs.n_kv_heads * cs.head_dim * esz * 2 + 4) + \
+                cs.n_heads * cs.head_dim * esz * 2
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"float64 decode of the first {len(done)} of {cs.batch} requests "
                       f"({int(cs.seq_lens[done].sum())} KV positions, history regenerated "
                       f"from the seeded streams), {dt:.1f} s"}
+
+
+def cpu_baseline_prefill(cs, budget_s: float = 10.0):
+    """The oracle on a bounded sample of the prefill workload: whole requests
+    in batch order until budget_s has passed, in GFLOP/s over the same
+    unmasked-pair count as the device figure."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import expect as E
+    from threadpoolctl import threadpool_limits
+    cores = _host_cores()
+    rot = E.rotated_new(cs)
+    done, flops = [], 0
+    with threadpool_limits(cores):
+        t0 = time.perf_counter()
+        for b in range(cs.batch):
+            E.expected_prefill(cs, sample=[b], rot=rot)
+            done.append(b)
+            e, p = int(cs.new_lens[b]), int(cs.prefix_lens[b])
+            flops += 4 * cs.head_dim * cs.n_heads * (e * p + e * (e + 1) // 2)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e9, 4), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 causal prefill of the first {len(done)} of {cs.batch} requests "
+                      f"({int(cs.new_lens[done].sum())} query rows, {flops / 1e9:.2f} GFLOP), {dt:.1f} s"}
 
 
 def _time_ms(fn, stream, reps: int = 10, warm: int = 2) -> float:
@@ -159,6 +197,134 @@ def _time_ms(fn, stream, reps: int = 10, warm: int = 2) -> float:
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def _rep_ms(fn, stream, reps: int = 50, warm: int = 3, flush=None) -> np.ndarray:
+    """Durations (ms) of `reps` separate calls of fn(), each bracketed by its
+    own pair of HIP events on `stream`.  With flush, flush() runs between
+    calls, outside the brackets.  A spin kernel goes first so that the calls
+    are queued ahead of the device and host launch time stays out."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda._sleep(40_000_000)
+    for a, b in ev:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def _stats(ms: np.ndarray) -> dict:
+    return {"median_us": round(float(np.median(ms)) * 1e3, 2), "mean_us": round(float(ms.mean()) * 1e3, 2),
+            "min_us": round(float(ms.min()) * 1e3, 2), "reps": int(ms.size)}
+
+
+def measure_small_configs(stream, dev):
+    """The workloads other than the two headline batches, each measured on its
+    own: median of 50 calls with warm caches, and with a 512 MB write
+    between calls (which evicts the 256 MB last-level cache)."""
+    import torch
+    import paged_gqa_attention_rope_amd as astr
+    import staging
+    from workloads import make_case
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: scratch.fill_(1)
+    out = {}
+    n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    # 1: tiny float32 decode, every position through the rotary write
+    cs = make_case(1)
+    st = staging.stage(cs, device=dev, canary=False)
+    q_dec = staging.decode_query(st)
+    res = {"workload": cs.name, "bound": "launch latency (50 tokens, 2 requests)"}
+    for label, fl in (("hot", None), ("flushed", flush)):
+        w = _rep_ms(lambda: staging.run_write(st), stream, flush=fl)
+        d = _rep_ms(lambda: staging.run_decode(st, q_dec), stream, flush=fl)
+        res[label] = {"rope_kv_write": _stats(w), "decode_attn": _stats(d)}
+    out["1"] = res
+    del st
+
+    # 2: 8-request decode whose whole working set fits the last-level cache
+    cs = make_case(2)
+    st = staging.stage(cs, device=dev, canary=False)
+    staging.run_write(st)
+    q_dec = staging.decode_query(st)
+    o_part, lse_part = astr.decode_workspace(st.attn_cache, cs.n_heads, cs.split_chunk)
+    outd = torch.empty_like(q_dec)
+    nbytes = decode_bytes(cs)
+    res = {"workload": cs.name, "bytes_per_launch": nbytes,
+           "bound": f"HBM in principle; the {nbytes / 1e6:.1f} MB working set fits the 256 MB last-level "
+                    "cache, so warm calls read it from there"}
+    for label, fl in (("hot", None), ("flushed", flush)):
+        d = _rep_ms(lambda: staging.run_decode(st, q_dec, out=outd, o_part=o_part, lse_part=lse_part), stream,
+                    flush=fl)
+        gbs = nbytes / (float(np.median(d)) * 1e-3) / 1e9
+        res[label] = {**_stats(d), "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    out["2"] = res
+    del st
+
+    # 3: 4-request contiguous prefill, no prefix
+    cs = make_case(3)
+    st = staging.stage(cs, device=dev, canary=False)
+    staging.run_write(st)
+    outp = torch.empty_like(st.q)
+    flops = prefill_flops(cs)
+    c = st.attn_cache
+    units = int(c.prefill_units.shape[0]) if c.prefill_units is not None else c.num_q_tiles
+    real = int((c.prefill_units[:, 6] > 0).sum()) if c.prefill_units is not None else c.num_q_tiles
+    wgs = real * (cs.n_heads // 4)
+    steps = [(-(-(int(p) + min(64 * (t + 1), int(e))) // 32)) for e, p in zip(cs.new_lens, cs.prefix_lens)
+             for t in range(-(-int(e) // 64))]
+    res = {"workload": cs.name, "flops_per_launch": flops,
+           "occupancy": {"query_tiles": c.num_q_tiles, "plan_units": units, "split_tiles": c.num_prefill_pairs,
+                         "workgroups": wgs, "compute_units": n_cus, "waves_per_workgroup": 8,
+                         "busy_cu_frac": round(min(wgs, n_cus) / n_cus, 3),
+                         "longest_tile_key_steps": max(steps), "mean_tile_key_steps": round(float(np.mean(steps)), 1)},
+           "bound": f"latency / occupancy: {wgs} workgroups (one per compute unit) for {n_cus} compute units, "
+                    f"and the longest tile walks {max(steps)} steps of 32 keys against a mean of "
+                    f"{np.mean(steps):.1f}"}
+    for label, fl in (("hot", None), ("flushed", flush)):
+        w = _rep_ms(lambda: staging.run_write(st), stream, flush=fl)
+        p = _rep_ms(lambda: staging.run_prefill(st, out=outp), stream, flush=fl)
+        tfs = flops / (float(np.median(p)) * 1e-3) / 1e12
+        res[label] = {"rope_kv_write": _stats(w), "prefill_attn": {**_stats(p), "TFLOPs": round(tfs, 1),
+                                                                  "frac_of_bf16_peak": round(tfs / BF16_PEAK_TFLOPS, 4)}}
+    out["3"] = res
+    del st, scratch
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_ceilings(stream, dev):
+    """What a plain streaming read (4 GiB, 16-byte loads) and a loop of
+    independent matrix-core products attain on this device."""
+    import torch
+    import paged_gqa_attention_rope_amd as astr
+    n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    buf = torch.ones(1 << 30, dtype=torch.float32, device=dev)            # 4 GiB
+    nbytes = buf.numel() * 4
+    res = {}
+    for nt in (True, False):
+        wg = 8 * n_cus
+        sink = torch.empty(wg, dtype=torch.int32, device=dev)
+        ms = _rep_ms(lambda: astr.ceiling_stream_read(buf, wg, nt, sink), stream, reps=20)
+        res["stream_read_nt" if nt else "stream_read"] = {
+            "GBps": round(nbytes / (float(np.median(ms)) * 1e-3) / 1e9, 1), "bytes": nbytes, **_stats(ms)}
+    del buf
+    wg, iters = 4 * n_cus, 4096                                           # 4 waves per SIMD
+    sink = torch.empty(256 * wg, dtype=torch.float32, device=dev)
+    flops = astr.ceiling_mfma_loop(wg, iters, sink)
+    ms = _rep_ms(lambda: astr.ceiling_mfma_loop(wg, iters, sink), stream, reps=20)
+    res["mfma_bf16_16x16x32"] = {"TFLOPs": round(flops / (float(np.median(ms)) * 1e-3) / 1e12, 1),
+                                 "flops": flops, "waves_per_simd": 4, **_stats(ms)}
+    torch.cuda.empty_cache()
+    return res
 
 
 def measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream, dbytes):
@@ -255,21 +421,49 @@ def measure_pagepool_lifecycle(n_requests=1536, batch=16, decode_steps=8, seed=6
             "pages_cached_at_end": pp.cached_pages()}
 
 
+def summarize_trace(trace_dir: str):
+    """Per-kernel call count, mean and median duration (us) from a rocprofv3
+    --kernel-trace run (its kernel_trace.csv), as a markdown table."""
+    import csv
+    import glob
+    rows = {}
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"].replace("void astr::(anonymous namespace)::", "")
+            if not any(k in name for k in ("decode", "prefill", "rope", "stream_read", "mfma_loop")):
+                continue
+            name = name.split("(")[0]
+            rows.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | calls | mean | median | min | max |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for name in sorted(rows):
+        v = np.array(rows[name])
+        print(f"| `{name}` | {v.size} | {v.mean():.2f} | {np.median(v):.2f} | {v.min():.2f} | {v.max():.2f} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline steps (no other workloads, ceilings or adjacent rows)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device-to-device copy (a reference dispatch of "
                          "known size for calibrating HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print per-kernel call counts, mean and median durations of a rocprofv3 "
+                         "--kernel-trace run and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -281,6 +475,9 @@ def main():
     import staging
     from workloads import make_case
 
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     t_stage = time.perf_counter()
@@ -288,8 +485,8 @@ def main():
     cs_p = make_case(4, args.seed)
     st_p = staging.stage(cs_p, device=dev, canary=False)
     st_d = staging.stage(cs_d, device=dev, canary=False)
-    print(f"[bench] staged decode ({cs_d.pool_slots} slots x {cs_d.n_layers} layers) and prefill "
-          f"in {time.perf_counter() - t_stage:.1f} s", file=sys.stderr, flush=True)
+    say(f"staged decode ({cs_d.pool_slots} slots x {cs_d.n_layers} layers) and prefill "
+        f"in {time.perf_counter() - t_stage:.1f} s")
     # host cost of one step's metadata build (decode: every request appends a token)
     t0 = time.perf_counter()
     st_d.pool.bind(st_d.reqs, np.ones(cs_d.batch, dtype=np.int32), 64)
@@ -339,6 +536,7 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    say(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
@@ -347,16 +545,34 @@ def main():
     parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
                       for i in range(args.steps)])             # ms
     t_wd, t_dec, t_wp, t_pre = parts.mean(axis=0)
+    m_wd, m_dec, m_wp, m_pre = np.median(parts, axis=0)
     dbytes = decode_bytes(cs_d)
     pflops = prefill_flops(cs_p)
     dec_gbs = dbytes / (t_dec * 1e-3) / 1e9
     pre_tfs = pflops / (t_pre * 1e-3) / 1e12
 
-    nxt = measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream, dbytes)
+    nxt = configs = ceilings = None
+    if not args.no_extras:
+        say("adjacent rows")
+        nxt = measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream, dbytes)
+        del st_d, o_part, lse_part
+        torch.cuda.empty_cache()
+        say("other workloads")
+        configs = measure_small_configs(stream, dev)
+        say("ceilings")
+        ceilings = measure_ceilings(stream, dev)
 
-    cpu = None
+    cpu = cpu_p = None
     if not args.no_cpu_baseline:
+        say("oracle baselines")
         cpu = cpu_baseline(cs_d)
+        cpu_p = cpu_baseline_prefill(cs_p)
+
+    def attainable(rate, key, unit):
+        if not ceilings:
+            return None
+        return {"ceiling": key, "attainable": ceilings[key][unit], "unit": "GB/s" if unit == "GBps" else "TFLOP/s",
+                "frac": round(rate / ceilings[key][unit], 4)}
 
     line = {
         "metric": "decode attn KV GB/s (% HBM peak) + prefill attn TFLOP/s (% bf16 MFMA peak)",
@@ -383,20 +599,30 @@ def main():
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("decode"),
                      "kernel": "decode_attn (split-K pass + merge)",
-                     "bytes_per_launch": dbytes, "ms_per_launch": round(float(t_dec), 5)},
+                     "bytes_per_launch": dbytes, "ms_per_launch": round(float(t_dec), 5),
+                     "median_ms_per_launch": round(float(m_dec), 5),
+                     "attainable": attainable(dec_gbs, "stream_read_nt", "GBps")},
         "prefill": {"value": round(pre_tfs, 2), "unit": "TFLOP/s",
                     "roofline": {"bound": "mfma", "achieved": round(pre_tfs, 2),
                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": round(pre_tfs / BF16_PEAK_TFLOPS, 4),
                                  "traffic": measured_traffic("prefill"),
                                  "kernel": "prefill_attn", "flops_per_launch": pflops,
-                                 "ms_per_launch": round(float(t_pre), 5)},
+                                 "ms_per_launch": round(float(t_pre), 5),
+                                 "median_ms_per_launch": round(float(m_pre), 5),
+                                 "attainable": attainable(pre_tfs, "mfma_bf16_16x16x32", "TFLOPs")},
                     "plan": {"units": 0 if st_p.attn_cache.prefill_units is None
                              else int(st_p.attn_cache.prefill_units.shape[0]),
-                             "split_tiles": int(st_p.attn_cache.num_prefill_pairs)}},
+                             "split_tiles": int(st_p.attn_cache.num_prefill_pairs)},
+                    "cpu_baseline": cpu_p},
         "parts_ms": {"rope_kv_write_decode": round(float(t_wd), 5), "decode_attn": round(float(t_dec), 5),
                      "rope_kv_write_prefill": round(float(t_wp), 5), "prefill_attn": round(float(t_pre), 5),
+                     "median": {"rope_kv_write_decode": round(float(m_wd), 5), "decode_attn": round(float(m_dec), 5),
+                                "rope_kv_write_prefill": round(float(m_wp), 5),
+                                "prefill_attn": round(float(m_pre), 5)},
                      "host_bind_decode": round(bind_ms, 3), "host_plan_prefill": round(plan_ms, 3)},
+        "configs": configs,
+        "ceilings": ceilings,
         "next": nxt,
         "cpu_baseline": cpu,
     }

@@ -1,4 +1,5 @@
-"""ctypes view of libastr.so: the prototypes of include/astr.h, nothing else."""
+"""ctypes view of libastr.so: the prototypes of include/astr.h and
+include/astr_ceiling.h, nothing else."""
 
 import ctypes
 import os
@@ -14,7 +15,7 @@ ASTR_E_LAUNCH = -4
 ASTR_F32 = 0
 ASTR_BF16 = 1
 
-# every symbol include/astr.h declares
+# every symbol include/*.h declares
 EXPORTS = (
     "astr_last_error", "astr_rope_table", "astr_rope_kv_write", "astr_rope_backward",
     "astr_decode_num_splits", "astr_decode_workspace_bytes", "astr_decode_split_items", "astr_decode_attn_write",
@@ -24,6 +25,8 @@ EXPORTS = (
     "astr_pagepool_release", "astr_pagepool_table", "astr_pagepool_free_pages",
     "astr_pagepool_page_ref", "astr_pagepool_complete", "astr_pagepool_evict",
     "astr_pagepool_cached_pages", "astr_pagepool_evicted_pages",
+    # include/astr_ceiling.h
+    "astr_ceiling_stream_read", "astr_ceiling_mfma_loop",
 )
 
 c_int, c_i32p, c_vp = ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
@@ -102,6 +105,8 @@ def lib():
     L.astr_pagepool_cached_pages.restype = ctypes.c_int64
     L.astr_pagepool_evicted_pages.argtypes = [c_vp]
     L.astr_pagepool_evicted_pages.restype = ctypes.c_int64
+    L.astr_ceiling_stream_read.argtypes = [c_vp, ctypes.c_size_t, c_int, c_int, c_vp, c_vp]
+    L.astr_ceiling_mfma_loop.argtypes = [c_int, c_int, c_vp, c_vp]
     _lib = L
     return L
 

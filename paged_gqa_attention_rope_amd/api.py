@@ -366,6 +366,30 @@ def prefill_attn(q: torch.Tensor, cache: KVCache, layer_id: int, sm_scale: float
 
 
 # ---------------------------------------------------------------------------
+# attainable-rate probes (include/astr_ceiling.h)
+# ---------------------------------------------------------------------------
+
+def ceiling_stream_read(buf: torch.Tensor, workgroups: int = 2048, nontemporal: bool = True,
+                        sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Read every byte of buf once (astr_ceiling_stream_read); returns the sink."""
+    _dev_tensor(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(workgroups, dtype=torch.int32, device=buf.device)
+    _dev_tensor(sink, "sink", torch.int32, buf.device, workgroups)
+    check(lib().astr_ceiling_stream_read(_vp(buf), nbytes, int(workgroups), int(bool(nontemporal)), _vp(sink),
+                                         _stream(buf)))
+    return sink
+
+
+def ceiling_mfma_loop(workgroups: int, iters: int, sink: torch.Tensor) -> int:
+    """Run the matrix-core loop (astr_ceiling_mfma_loop); returns its flop count."""
+    _dev_tensor(sink, "sink", torch.float32, None, 256 * workgroups)
+    check(lib().astr_ceiling_mfma_loop(int(workgroups), int(iters), _vp(sink), _stream(sink)))
+    return 2 * 16 * 16 * 32 * 8 * int(iters) * 4 * int(workgroups)
+
+
+# ---------------------------------------------------------------------------
 # the host page-table builder
 # ---------------------------------------------------------------------------
 

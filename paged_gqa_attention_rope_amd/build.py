@@ -25,7 +25,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 GXX = os.environ.get("CXX", "g++")
 
-HIP_SOURCES = ["rope.hip", "decode.hip", "prefill.hip"]
+HIP_SOURCES = ["rope.hip", "decode.hip", "prefill.hip", "ceiling.hip"]
 # per-source extra flags: the attention kernels never rely on NaN propagation
 # (masking uses -inf, which stays honoured), and without it every fmaxf of a
 # matrix-core result is preceded by a NaN-quieting canonicalisation

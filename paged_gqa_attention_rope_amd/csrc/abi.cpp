@@ -10,6 +10,7 @@
 #include <cstdio>
 
 #include "astr.h"
+#include "astr_ceiling.h"
 #include "kernels.hpp"
 #include "status.hpp"
 
@@ -328,4 +329,20 @@ extern "C" size_t astr_prefill_workspace_bytes(int pairs, int n_heads, int head_
     if (pairs == 0) return 0;
     const int64_t slots = astr::prefill_part_slots(pairs, n_heads);
     return static_cast<size_t>(astr::prefill_counts_bytes(slots) + slots * 2 * astr::kPrefillPartFloats * 4);
+}
+
+extern "C" int astr_ceiling_stream_read(const void *buf, size_t bytes, int workgroups, int nontemporal,
+                                        uint32_t *sink, void *stream) {
+    if (!buf || !sink || workgroups < 1 || bytes < 16 || bytes % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+        return fail(ASTR_E_INVAL, "ceiling_stream_read: bad argument");
+    return astr::launched("ceiling_stream_read",
+                          astr::launch_ceiling_stream_read(buf, bytes, workgroups, nontemporal != 0, sink,
+                                                           static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int astr_ceiling_mfma_loop(int workgroups, int iters, float *sink, void *stream) {
+    if (!sink || workgroups < 1 || iters < 1) return fail(ASTR_E_INVAL, "ceiling_mfma_loop: bad argument");
+    return astr::launched("ceiling_mfma_loop",
+                          astr::launch_ceiling_mfma_loop(workgroups, iters, sink, static_cast<hipStream_t>(stream)));
 }

@@ -101,5 +101,8 @@ hipError_t launch_rope_backward(void *grad, const int32_t *positions, int n_toke
                                 int dtype, const float *freqs, int max_pos, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_ceiling_stream_read(const void *buf, uint64_t bytes, int workgroups, bool nontemporal,
+                                      uint32_t *sink, hipStream_t s);
+hipError_t launch_ceiling_mfma_loop(int workgroups, int iters, float *sink, hipStream_t s);
 
 }  // namespace astr

@@ -30,8 +30,11 @@ def _lib():
 
 def test_library_exports_every_declared_symbol():
     L = _lib()
-    header = open(os.path.join(ROOT, "include", "astr.h")).read()
-    declared = set(re.findall(r"\b(astr_[a-z_0-9]+)\s*\(", header))
+    inc = os.path.join(ROOT, "include")
+    declared = set()
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            declared |= set(re.findall(r"\b(astr_[a-z_0-9]+)\s*\(", open(os.path.join(inc, h)).read()))
     assert declared == set(L.EXPORTS)
     so = ctypes.CDLL(L.LIB_PATH)
     for name in declared:
