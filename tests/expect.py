@@ -64,18 +64,29 @@ def request_kv(cs, b: int, k_rot: np.ndarray):
     return (np.concatenate([kh.astype(np.float64), kn]), np.concatenate([vh.astype(np.float64), vn]))
 
 
-def expected_decode(cs, sample=None, rot=None, key_ok=None):
+def expected_decode(cs, sample=None, rot=None, key_ok=None, workers: int = 1):
     """{b: [Hq, D]} for the newest token of each sampled request (key_ok:
-    {b: bool [L_b]} marks the keys that take part, default all)."""
+    {b: bool [L_b]} marks the keys that take part, default all).  With
+    workers > 1 the requests are spread over that many threads (the oracle's
+    NumPy work releases the interpreter lock; BLAS runs one thread each)."""
     q_rot, k_rot = rot if rot is not None else rotated_new(cs)
     off = new_offsets(cs)
     scale = 1.0 / math.sqrt(cs.head_dim)
-    out = {}
-    for b in (range(cs.batch) if sample is None else sample):
+    todo = list(range(cs.batch) if sample is None else sample)
+
+    def one(b):
         K, V = request_kv(cs, b, k_rot)
         ok = None if key_ok is None else key_ok.get(b)
-        out[b] = A.decode_dense(q_rot[off[b + 1] - 1], K, V, scale, ok)
-    return out
+        return b, A.decode_dense(q_rot[off[b + 1] - 1], K, V, scale, ok)
+
+    if workers <= 1:
+        return dict(one(b) for b in todo)
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    # longest first, so that no long request starts last
+    todo.sort(key=lambda b: -int(cs.seq_lens[b]))
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=workers) as ex:
+        return dict(ex.map(one, todo))
 
 
 def expected_prefill(cs, sample=None, rot=None, key_ok=None):
