@@ -94,7 +94,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] == counter:
-                    name = r["Kernel_Name"].replace("void astr::(anonymous namespace)::", "")
+                    name = r["Kernel_Name"].replace("void ", "", 1).replace("astr::(anonymous namespace)::", "", 1)
                     vals.setdefault(name, []).append(float(r["Counter_Value"]))
         return vals
 
@@ -429,7 +429,7 @@ def summarize_trace(trace_dir: str):
     rows = {}
     for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
-            name = r["Kernel_Name"].replace("void astr::(anonymous namespace)::", "")
+            name = r["Kernel_Name"].replace("void ", "", 1).replace("astr::(anonymous namespace)::", "", 1)
             if not any(k in name for k in ("decode", "prefill", "rope", "stream_read", "mfma_loop")):
                 continue
             name = name.split("(")[0]

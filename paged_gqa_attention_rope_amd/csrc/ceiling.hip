@@ -48,20 +48,36 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
     if (threadIdx.x == 0) sink[blockIdx.x] = w[0] ^ w[1] ^ w[2] ^ w[3];
 }
 
+// A bf16 pair with random signs and mantissas and magnitudes in about
+// [2^-7, 2^2): operands whose bits toggle like real activations do (the
+// matrix cores draw more power, and the clock drops further, than with
+// constant or mostly-zero operands).
+__device__ __forceinline__ uint32_t random_bf16_pair(uint32_t x) {
+    x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+    const uint32_t lo = (x & 0x807fu) | ((120u + (x >> 8) % 9u) << 7);
+    const uint32_t hi = ((x >> 16) & 0x807fu) | ((120u + (x >> 24) % 9u) << 7);
+    return lo | (hi << 16);
+}
+
 // Each wave keeps 8 independent accumulators and issues 8 products per
-// iteration from operands held in registers (built from the lane index so
-// that they are not constants).  One store per lane at the end.
+// iteration from operands held in registers.  The accumulators start from
+// distinct values: started from one shared constant, the compiler rotates
+// them through overlapping registers, which chains the products.  One store
+// per lane at the end.
 __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float *__restrict__ sink) {
     Frag8 a, b;
-    const uint32_t l = threadIdx.x & 63;
+    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        a.w[e] = 0x3f803f80u ^ ((l + e) & 7);            // ~1.0 with a varying low bit
-        b.w[e] = 0x3c003c00u ^ ((l * 3 + e) & 7);        // ~2^-7
+        a.w[e] = random_bf16_pair(8u * t + e);
+        b.w[e] = random_bf16_pair(8u * t + 4u + e);
     }
     f32x4_t acc[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 8; ++k) {
+        const float x = static_cast<float>(threadIdx.x * 8 + k);
+        acc[k] = f32x4_t{x, x + 1.f, x + 2.f, x + 3.f};
+    }
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[k] = mfma16(a, b, acc[k]);
