@@ -260,6 +260,27 @@ int astr_decode_attn(const void *q, int n_heads, const astr_kv_meta *m, int laye
                      void *out, astr_dtype act_dtype, void *stream);
 
 /*
+ * astr_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with the split-K scratch
+ * taken from a device array that the library holds in file scope, one copy
+ * per GPU, 160 MiB (ASTR_DECODE_STATIC_SCRATCH_BYTES), placed when the
+ * library's code is loaded on that GPU and kept until the process ends.
+ * The call itself allocates nothing and frees nothing; the caller passes
+ * only q, out and the metadata.  A call whose scratch
+ * (astr_decode_workspace_bytes) exceeds the array returns ASTR_E_INVAL
+ * before anything is launched.  Every call on one GPU uses that GPU's one
+ * array: calls that overlap on one GPU (several streams or threads) race
+ * and must be serialised by the caller.  Nothing in the array needs to
+ * start at zero: each split's partials are written before the merge reads
+ * them.  Arguments and errors as astr_decode_attn.
+ */
+#define ASTR_DECODE_STATIC_SCRATCH_BYTES ((size_t)160 << 20)
+int astr_decode_attn_noalloc(const void *q, int n_heads, const astr_kv_meta *m, int layer_id,
+                             int split_chunk, float sm_scale, void *out, astr_dtype act_dtype,
+                             void *stream);
+
+/*
  * The decode step with its rotary write fused in (inference.md, "Attention
  * Backend": the paged decode op is handed the step's new k and v and writes
  * them to the cache itself; internals.md, "KV Cache Mathematics": RoPE is

@@ -7,7 +7,7 @@ error, never a fallback.
 """
 
 from .api import (  # noqa: F401
-    KVCache, PagePool, cache_from_bind, ceiling_mfma_loop, ceiling_stream_read, decode_attn, decode_attn_write, decode_num_splits, decode_split_items,
+    KVCache, PagePool, cache_from_bind, ceiling_mfma_loop, ceiling_stream_read, decode_attn, decode_attn_noalloc, decode_attn_write, decode_num_splits, decode_split_items,
     decode_workspace, decode_workspace_bytes,
     prefill_attn, prefill_plan, prefill_workspace_bytes, rope_backward, rope_kv_write, rope_table,
 )

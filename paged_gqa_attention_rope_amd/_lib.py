@@ -19,7 +19,7 @@ ASTR_BF16 = 1
 EXPORTS = (
     "astr_last_error", "astr_rope_table", "astr_rope_kv_write", "astr_rope_backward",
     "astr_decode_num_splits", "astr_decode_workspace_bytes", "astr_decode_split_items", "astr_decode_attn_write",
-    "astr_decode_attn", "astr_prefill_attn", "astr_prefill_workspace_bytes", "astr_prefill_plan",
+    "astr_decode_attn", "astr_decode_attn_noalloc", "astr_prefill_attn", "astr_prefill_workspace_bytes", "astr_prefill_plan",
     "astr_pagepool_create", "astr_pagepool_destroy",
     "astr_pagepool_admit", "astr_pagepool_extend", "astr_pagepool_bind", "astr_pagepool_insert",
     "astr_pagepool_release", "astr_pagepool_table", "astr_pagepool_free_pages",
@@ -74,6 +74,8 @@ def lib():
     L.astr_decode_split_items.argtypes = [c_i32p, c_int, c_int, c_i32p, c_i32p, c_int, ctypes.POINTER(c_int)]
     L.astr_decode_attn.argtypes = [c_vp, c_int, ctypes.POINTER(KvMeta), c_int, c_int, ctypes.c_float,
                                    c_vp, c_vp, c_vp, c_int, c_vp]
+    L.astr_decode_attn_noalloc.argtypes = [c_vp, c_int, ctypes.POINTER(KvMeta), c_int, c_int, ctypes.c_float,
+                                           c_vp, c_int, c_vp]
     L.astr_decode_attn_write.argtypes = [c_vp, c_vp, c_vp, c_int, ctypes.POINTER(KvMeta), c_int, c_vp, c_int,
                                          c_int, ctypes.c_float, c_vp, c_vp, c_vp, c_int, c_vp]
     L.astr_prefill_attn.argtypes = [c_vp, c_int, c_int, ctypes.POINTER(KvMeta), c_int, ctypes.c_float,

@@ -314,6 +314,23 @@ def decode_attn(q: torch.Tensor, cache: KVCache, layer_id: int, split_chunk: int
     return out
 
 
+def decode_attn_noalloc(q: torch.Tensor, cache: KVCache, layer_id: int, split_chunk: int,
+                        sm_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode_attn with the split-K scratch in the library's static device array
+    (astr_decode_attn_noalloc): the call allocates nothing when out is given."""
+    m = _meta(cache)
+    kb = cache.k_buffer
+    b, d = cache.batch, int(kb.shape[3])
+    _need(q.dim() == 3 and q.shape[0] == b and q.shape[2] == d, "q must be [batch, n_heads, head_dim]")
+    _dev_tensor(q, "q", kb.dtype, kb.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor(out, "out", kb.dtype, kb.device, q.numel())
+    check(lib().astr_decode_attn_noalloc(_vp(q), int(q.shape[1]), ctypes.byref(m), int(layer_id), int(split_chunk),
+                                         float(sm_scale), _vp(out), _DTYPES[q.dtype], _stream(q)))
+    return out
+
+
 def decode_attn_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: KVCache,
                       layer_id: int, freqs_cis: torch.Tensor, split_chunk: int, sm_scale: float = 0.0,
                       out: Optional[torch.Tensor] = None, o_part: Optional[torch.Tensor] = None,

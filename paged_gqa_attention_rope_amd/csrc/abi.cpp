@@ -231,6 +231,36 @@ extern "C" int astr_decode_attn(const void *q, int n_heads, const astr_kv_meta *
     return astr::launched("decode_attn", astr::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+static_assert(astr::kStaticDecodeScratchBytes == ASTR_DECODE_STATIC_SCRATCH_BYTES,
+              "the header states the static scratch size");
+
+extern "C" int astr_decode_attn_noalloc(const void *q, int n_heads, const astr_kv_meta *m, int layer_id,
+                                        int split_chunk, float sm_scale, void *out, astr_dtype act_dtype,
+                                        void *stream) {
+    if (!m) return fail(ASTR_E_INVAL, "decode_attn_noalloc: null meta");
+    float *o_part = nullptr, *lse_part = nullptr;
+    const size_t need = astr_decode_workspace_bytes(m->batch, n_heads, m->head_dim, m->max_len, split_chunk);
+    if (need > astr::kStaticDecodeScratchBytes)
+        return fail(ASTR_E_INVAL,
+                    "decode_attn_noalloc: the split-K scratch needs %zu bytes, the static scratch holds %zu "
+                    "(use astr_decode_attn with a caller-owned workspace, or a larger split_chunk)",
+                    need, astr::kStaticDecodeScratchBytes);
+    if (need > 0) {
+        const hipError_t e = astr::static_decode_scratch(&o_part);
+        if (e != hipSuccess)
+            return fail(ASTR_E_LAUNCH, "decode_attn_noalloc: static scratch: %s", hipGetErrorString(e));
+        const size_t rows = static_cast<size_t>(m->batch) * n_heads *
+                            astr_decode_num_splits(m->max_len, split_chunk);
+        lse_part = o_part + rows * m->head_dim;
+    }
+    astr::DecodeArgs a{};
+    bool empty;
+    const int st = decode_args("decode_attn_noalloc", q, out, n_heads, m, layer_id, split_chunk, sm_scale, o_part,
+                               lse_part, act_dtype, a, empty);
+    if (st || empty) return st;
+    return astr::launched("decode_attn_noalloc", astr::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int astr_decode_attn_write(const void *q, const void *k_new, const void *v_new, int n_heads,
                                       const astr_kv_meta *m, int layer_id, const float *freqs_cis, int max_pos,
                                       int split_chunk, float sm_scale, float *o_part, float *lse_part,

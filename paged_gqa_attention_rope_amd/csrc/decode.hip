@@ -26,6 +26,8 @@
 // o = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M), over the request's
 // ceil(L_b / C) splits.  When the batch has a single split the first pass
 // writes the output directly and pass 2 is not launched.
+#include <mutex>
+
 #include "device.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
@@ -610,6 +612,33 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const bool bf = a.pool.dtype == 1;
     if (a.pool.head_dim == 128) return bf ? launch_decode_g<bf16_t, 128>(a, s) : launch_decode_g<float, 128>(a, s);
     return bf ? launch_decode_g<bf16_t, 64>(a, s) : launch_decode_g<float, 64>(a, s);
+}
+
+// Split-K scratch for callers that cannot allocate: a file-scope device
+// array, one copy per GPU (the runtime places it when it loads this code
+// object on a device; it stays until the process ends).  Host code must not
+// pass `scratch` itself to a kernel -- on the host that name is a stand-in,
+// not a device address -- but the address hipGetSymbolAddress returns for
+// the current device, looked up once per device and kept.
+static __device__ __align__(256) float scratch[kStaticDecodeScratchBytes / sizeof(float)];
+
+hipError_t static_decode_scratch(float **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float *by_device[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!by_device[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        by_device[dev] = static_cast<float *>(p);
+    }
+    *ptr = by_device[dev];
+    return hipSuccess;
 }
 
 }  // namespace astr

@@ -100,6 +100,10 @@ hipError_t launch_rope_kv_write(const RopeArgs &a, hipStream_t s);
 hipError_t launch_rope_backward(void *grad, const int32_t *positions, int n_tokens, int n_heads, int head_dim,
                                 int dtype, const float *freqs, int max_pos, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+// Capacity of the file-scope split-K scratch of the allocation-free decode,
+// and its address on the current device (looked up once per device).
+constexpr size_t kStaticDecodeScratchBytes = size_t(160) << 20;
+hipError_t static_decode_scratch(float **ptr);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_ceiling_stream_read(const void *buf, uint64_t bytes, int workgroups, bool nontemporal,
                                       uint32_t *sink, hipStream_t s);

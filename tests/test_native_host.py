@@ -364,6 +364,25 @@ def test_activation_dtype_must_match_the_pool():
         assert b"act_dtype" in so.astr_last_error()
 
 
+def test_noalloc_decode_rejects_scratch_beyond_its_array():
+    """The allocation-free decode checks its scratch size on the host before
+    touching the device: 256 requests x 16 heads x 128 splits of a 128-wide
+    head need 270 MB, more than the 160 MiB static array."""
+    L = _lib()
+    so = L.lib()
+    m = L.KvMeta()
+    m.k_buffer = m.v_buffer = 0x1000
+    m.pool_slots, m.n_layers, m.n_kv_heads, m.head_dim, m.kv_dtype = 1 << 20, 1, 4, 128, L.ASTR_BF16
+    m.req_to_token = m.req_pool_indices = m.kv_indptr = 0x4000
+    m.num_reqs, m.max_ctx_len, m.batch, m.max_len = 256, 32768, 256, 32768
+    q = ctypes.c_void_p(0x2000)
+    need = so.astr_decode_workspace_bytes(256, 16, 128, 32768, 256)
+    assert need > 160 << 20
+    st = so.astr_decode_attn_noalloc(q, 16, ctypes.byref(m), 0, 256, 0.0, q, L.ASTR_BF16, None)
+    assert st == L.ASTR_E_INVAL and b"static scratch holds" in so.astr_last_error()
+    assert so.astr_decode_attn_noalloc(q, 16, None, 0, 256, 0.0, q, L.ASTR_BF16, None) == L.ASTR_E_INVAL
+
+
 def test_decode_workspace_bytes():
     """The split-K scratch: float32 o_part [B, H, S, D] then lse_part [B, H, S],
     S = ceil(max_len / chunk); nothing when one split covers max_len."""
