@@ -564,27 +564,30 @@ constexpr double kWhole = 7.0;             // per whole tile: prologue and outpu
 constexpr double kLower = 8.5;             // lower half: prologue and publishing its state
 constexpr double kUpper = 9.5;             // upper half: prologue, merge and output
 constexpr double kEmpty = 0.1;             // a tile the kernel skips
+constexpr int kJoinCap = 3;                // most units of one request an XCD takes by preference
 
 struct PlanUnit {
     double cost;
     int tile, piece;                       // piece -1: whole tile (or padding when tile is -1)
     int lo, hi;                            // key steps [lo, hi)
+    int group;                             // the tile's batch entry (its request)
 };
 
 // Units of the tiles, those marked in `split` cut in two halves at h =
 // max(1, floor(n * num / den)) steps, by decreasing cost (ties: tile order,
 // then lower half first).
-std::vector<PlanUnit> plan_units(const std::vector<int> &steps, const std::vector<char> &split, int num, int den) {
+std::vector<PlanUnit> plan_units(const std::vector<int> &steps, const std::vector<int> &group,
+                                 const std::vector<char> &split, int num, int den) {
     std::vector<PlanUnit> list;
     list.reserve(2 * steps.size());
     for (int t = 0; t < static_cast<int>(steps.size()); ++t) {
         const int n = steps[t];
         if (split[t] && n >= 2) {
             const int h = std::max(1, static_cast<int>(static_cast<int64_t>(n) * num / den));
-            list.push_back({kLower + h, t, 0, 0, h});
-            list.push_back({kUpper + (n - h), t, 1, h, INT32_MAX});
+            list.push_back({kLower + h, t, 0, 0, h, group[t]});
+            list.push_back({kUpper + (n - h), t, 1, h, INT32_MAX, group[t]});
         } else {
-            list.push_back({n > 0 ? kWhole + n : kEmpty, t, -1, 0, INT32_MAX});
+            list.push_back({n > 0 ? kWhole + n : kEmpty, t, -1, 0, INT32_MAX, group[t]});
         }
     }
     std::stable_sort(list.begin(), list.end(), [](const PlanUnit &a, const PlanUnit &b) {
@@ -595,31 +598,45 @@ std::vector<PlanUnit> plan_units(const std::vector<int> &steps, const std::vecto
     return list;
 }
 
-// Deal a cost-ordered list to the XCDs: each unit goes to the XCD where it
-// would end first (ties: fewer units queued, then the lower XCD); an XCD
-// runs its queue in order on cus_per_xcd compute units, one workgroup per
-// compute unit, the unit's wg_per_unit workgroups on the ones free first.
-// Returns the simulated end; queue[x] receives the units of XCD x.
-double deal(const std::vector<PlanUnit> &list, int wg_per_unit, int cus_per_xcd,
+// Deal a cost-ordered list to the XCDs: each unit goes to an XCD where it
+// would end first; among those, one that already holds at least one and
+// fewer than kJoinCap units of the same request comes first (it can serve
+// the request's keys and values from its own L2), then the one with fewer
+// units queued, then the lower XCD.  An XCD runs its queue in order on
+// cus_per_xcd compute units, one workgroup per compute unit, the unit's
+// wg_per_unit workgroups on the ones free first.  Returns the simulated end;
+// queue[x] receives the units of XCD x.
+double deal(const std::vector<PlanUnit> &list, int wg_per_unit, int cus_per_xcd, int groups,
             std::vector<std::vector<int>> &queue) {
     // free times of each XCD's compute units, ascending
     std::vector<std::vector<double>> free_at(kPlanXcds, std::vector<double>(cus_per_xcd, 0.0));
     std::vector<double> merged(cus_per_xcd);
+    // units of each request dealt to each XCD so far
+    std::vector<std::vector<int>> holds(kPlanXcds, std::vector<int>(std::max(groups, 1), 0));
     queue.assign(kPlanXcds, {});
     const int wg = std::min(wg_per_unit, cus_per_xcd);
     double end = 0.0;
     for (int i = 0; i < static_cast<int>(list.size()); ++i) {
         const double c = list[i].cost;
-        int best = 0;
+        const int grp = list[i].group;
+        int best = -1;
         double best_end = 0.0;
+        bool best_joins = false;
         for (int x = 0; x < kPlanXcds; ++x) {
             // the unit's last workgroup starts when its wg-th compute unit frees
             const double e = free_at[x][wg - 1] + c;
-            if (x == 0 || e < best_end || (e == best_end && queue[x].size() < queue[best].size())) {
+            const bool joins = grp >= 0 && holds[x][grp] > 0 && holds[x][grp] < kJoinCap;
+            bool take = best < 0 || e < best_end;
+            if (!take && e == best_end)
+                take = (joins && !best_joins) ||
+                       (joins == best_joins && queue[x].size() < queue[best].size());
+            if (take) {
                 best = x;
                 best_end = e;
+                best_joins = joins;
             }
         }
+        if (grp >= 0) ++holds[best][grp];
         // the k compute units free first take a workgroup each: their times
         // grow by c and merge back into the sorted rest
         std::vector<double> &f = free_at[best];
@@ -649,7 +666,7 @@ extern "C" int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_ind
         return astr::fail(ASTR_E_INVAL, "prefill_plan: bad argument");
     // key steps seen by each tile (0 for a tile the kernel skips), and its
     // request row, first query row, rows and first row's position
-    std::vector<int> steps(num_q_tiles, 0);
+    std::vector<int> steps(num_q_tiles, 0), group(num_q_tiles, -1);
     std::vector<std::array<int32_t, 4>> rows_of(num_q_tiles, {0, 0, 0, 0});
     int max_steps = 0;
     for (int t = 0; t < num_q_tiles; ++t) {
@@ -665,6 +682,7 @@ extern "C" int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_ind
         const int64_t q_row = qo_indptr[b] + row0;
         if (kv_end > INT32_MAX || q_row > INT32_MAX) continue;
         steps[t] = static_cast<int>((kv_end + kPlanStep - 1) / kPlanStep);
+        group[t] = b;
         rows_of[t] = {req_pool_indices[b], static_cast<int32_t>(q_row), static_cast<int32_t>(rows),
                       static_cast<int32_t>(p + row0)};
         max_steps = std::max(max_steps, steps[t]);
@@ -693,14 +711,14 @@ extern "C" int astr_prefill_plan(const int32_t *qo_indptr, const int32_t *kv_ind
         cands.push_back(std::move(c));
     }
     std::vector<std::vector<int>> queue, cand_queue;
-    std::vector<PlanUnit> best = plan_units(steps, std::vector<char>(num_q_tiles, 0), 1, 2);
-    const double base_end = deal(best, workgroups_per_tile, cus_per_xcd, queue);
+    std::vector<PlanUnit> best = plan_units(steps, group, std::vector<char>(num_q_tiles, 0), 1, 2);
+    const double base_end = deal(best, workgroups_per_tile, cus_per_xcd, batch, queue);
     double best_end = base_end;
     std::vector<PlanUnit> chosen;
     std::vector<std::vector<int>> chosen_queue;
     for (const Candidate &c : cands) {
-        std::vector<PlanUnit> cand = plan_units(steps, c.split, c.num, c.den);
-        const double end = deal(cand, workgroups_per_tile, cus_per_xcd, cand_queue);
+        std::vector<PlanUnit> cand = plan_units(steps, group, c.split, c.num, c.den);
+        const double end = deal(cand, workgroups_per_tile, cus_per_xcd, batch, cand_queue);
         if (end < best_end) {
             best_end = end;
             chosen.swap(cand);

@@ -480,13 +480,14 @@ def _plan_rule(meta, wg, num_cus):
     """The prefill work plan stated as its documented rule, in Python."""
     qo, kv, rpi = meta["qo_indptr"], meta["kv_indptr"], meta["req_pool_indices"]
     qt = meta["q_tile"]
-    steps, rows_of = [], []
+    steps, rows_of, group = [], [], []
     for b, i in zip(meta["q_tile_to_batch"], meta["q_tile_to_index"]):
         e = int(qo[b + 1] - qo[b])
         p = int(kv[b + 1] - kv[b]) - e
         row0 = int(i) * qt
         ok = e > 0 and p >= 0 and row0 < e
         steps.append(-(-(p + row0 + min(qt, e - row0)) // 32) if ok else 0)
+        group.append(int(b) if ok else -1)
         rows_of.append([int(rpi[b]), int(qo[b]) + row0, min(qt, e - row0), p + row0] if ok else [0, 0, 0, 0])
     big = 2 ** 31 - 1
 
@@ -501,12 +502,20 @@ def _plan_rule(meta, wg, num_cus):
         return sorted(out, key=lambda u: (-u[0], u[1], u[2]))
 
     def deal(lst):
+        # earliest end; on ties an XCD holding 1 or 2 units of the same
+        # request first, then fewer units queued, then the lower XCD
         free = [[0.0] * (num_cus // 8) for _ in range(8)]
         queue = [[] for _ in range(8)]
+        holds = [dict() for _ in range(8)]
         end = 0.0
         w = min(wg, num_cus // 8)
         for u in lst:
-            x = min(range(8), key=lambda x: (sorted(free[x])[w - 1] + u[0], len(queue[x]), x))
+            ends = [sorted(free[x])[w - 1] + u[0] for x in range(8)]
+            grp = group[u[1]]
+            joins = [grp >= 0 and 0 < holds[x].get(grp, 0) < 3 for x in range(8)]
+            x = min(range(8), key=lambda x: (ends[x], 0 if joins[x] else 1, len(queue[x]), x))
+            if grp >= 0:
+                holds[x][grp] = holds[x].get(grp, 0) + 1
             for _ in range(wg):
                 f = sorted(free[x])
                 f[0] += u[0]
@@ -594,7 +603,9 @@ def test_prefill_plan_splits_only_what_dominates():
     seq = np.concatenate([[2560], np.full(300, 200)])
     ext = np.concatenate([[64], np.full(300, 64)])
     units, pairs = astr.prefill_plan(_plan_meta(seq, ext), 16)
-    assert pairs == 1 and units[0][0] == 0 and units[1][0] == 0     # both halves first, on XCDs 0 and 1
+    # both halves lead XCD 0's queue (positions 0 and 8: its first two units),
+    # which has room for both at once; they stay together on one L2
+    assert pairs == 1 and units[0][0] == 0 and units[8][0] == 0 and (units[1:8, 0] != 0).all()
     assert astr.prefill_workspace_bytes(0, 16, 128) == 0
     per = 2 * (8 * 2 * 8 * 64 * 4 + 8 * 2 * 64 * 2) * 4
     assert astr.prefill_workspace_bytes(3, 16, 128) == 256 + 12 * per
@@ -608,13 +619,17 @@ def test_prefill_plan_errors_and_abi_checks():
     meta = _plan_meta([100, 300], [50, 200])
     p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     n, pr = ctypes.c_int(), ctypes.c_int()
-    u = np.zeros((8, 8), np.int32)
+    cap = 16 * meta["num_q_tiles"]                     # documented to always suffice
+    u = np.zeros((cap, 8), np.int32)
     args = [p(meta["qo_indptr"]), p(meta["kv_indptr"]), p(meta["req_pool_indices"]), 2,
             p(meta["q_tile_to_batch"]), p(meta["q_tile_to_index"]), meta["num_q_tiles"], 64]
-    assert so.astr_prefill_plan(*args, 4, 256, p(u), 8, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_OK
-    assert so.astr_prefill_plan(*args, 4, 4, p(u), 8, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
-    assert so.astr_prefill_plan(*args, 0, 256, p(u), 8, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
-    assert so.astr_prefill_plan(*args, 4, 256, p(u), 7, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
+    assert so.astr_prefill_plan(*args, 4, 256, p(u), cap, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_OK
+    need = n.value
+    assert need % 8 == 0 and 8 <= need <= cap
+    assert so.astr_prefill_plan(*args, 4, 256, p(u), need, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_OK
+    assert so.astr_prefill_plan(*args, 4, 4, p(u), cap, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
+    assert so.astr_prefill_plan(*args, 0, 256, p(u), cap, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
+    assert so.astr_prefill_plan(*args, 4, 256, p(u), need - 1, ctypes.byref(n), ctypes.byref(pr)) == L.ASTR_E_INVAL
     # the prefill call checks the plan before anything is launched
     m = L.KvMeta()
     m.k_buffer = m.v_buffer = 0x1000
