@@ -58,16 +58,22 @@ def prefill_flops(cs) -> int:
 
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_JSON = os.path.join(PROFILES, "hbm_traffic.json")
-KERNEL_SOURCES = {"decode": "paged_gqa_attention_rope_amd/csrc/decode.hip",
-                  "prefill": "paged_gqa_attention_rope_amd/csrc/prefill.hip"}
+# sources whose change invalidates a call's counter figures (the prefill's
+# traffic also depends on how its work plan places tiles on the XCDs)
+KERNEL_SOURCES = {"decode": ("paged_gqa_attention_rope_amd/csrc/decode.hip",),
+                  "prefill": ("paged_gqa_attention_rope_amd/csrc/prefill.hip",
+                              "paged_gqa_attention_rope_amd/csrc/pagepool.cpp")}
 # kernels (name prefixes in the rocprofv3 counter CSV) that make up each call
 CALL_KERNELS = {"decode": ("decode_mfma_kernel<128, 4, false>", "decode_merge_kernel<astr::bf16_t, 128>"),
                 "prefill": ("prefill_rs_kernel<4, false>",)}
 
 
-def _sha(path: str) -> str:
+def _sha(paths) -> str:
     import hashlib
-    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(os.path.join(ROOT, path), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(call: str):
@@ -90,18 +96,20 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
     import glob
 
     def per_kernel(d, counter):
+        # (kernel, grid in work-items) -> counter values: the same kernel runs
+        # on the headline workloads and on smaller ones in one bench run
         vals = {}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] == counter:
-                    name = r["Kernel_Name"].replace("void ", "", 1).replace("astr::(anonymous namespace)::", "", 1)
-                    vals.setdefault(name, []).append(float(r["Counter_Value"]))
+                    vals.setdefault((_short_name(r["Kernel_Name"]), int(r["Grid_Size"])), []).append(
+                        float(r["Counter_Value"]))
         return vals
 
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         v = per_kernel(d, counter)
-        copy = max(v.get("__amd_rocclr_copyBuffer", [0.0]))
+        copy = max([max(x) for (name, _), x in v.items() if name.startswith("__amd_rocclr_copyBuffer")] or [0.0])
         if copy <= 0:
             raise SystemExit(f"no copy-probe dispatch in {d}")
         scale = 2 ** 30 / (copy * 1024.0)          # bytes per counter KiB
@@ -109,12 +117,16 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
             rec = out.setdefault(call, {"source_sha": _sha(KERNEL_SOURCES[call]), "kernels": {}})
             total = 0.0
             for k in kernels:
-                match = [x for name, x in v.items() if name.startswith(k)]
+                # the headline workload is the largest launch of each kernel
+                match = sorted(((grid, x) for (name, grid), x in v.items() if name.startswith(k)),
+                               key=lambda gx: gx[0])
                 if not match:
                     raise SystemExit(f"no {k} dispatch in {d}")
-                kib = sum(match[0]) / len(match[0])
+                grid, x = match[-1]
+                kib = float(np.median(x))
                 rec["kernels"].setdefault(k, {})[counter] = {"kib_per_dispatch": round(kib, 1),
-                                                              "bytes": int(kib * 1024 * scale)}
+                                                              "bytes": int(kib * 1024 * scale),
+                                                              "grid": grid, "dispatches": len(x)}
                 total += kib * 1024 * scale
             rec["fetch_bytes" if counter == "FETCH_SIZE" else "write_bytes"] = int(total)
             rec[f"{counter.lower()}_scale"] = round(scale, 5)
@@ -421,24 +433,55 @@ def measure_pagepool_lifecycle(n_requests=1536, batch=16, decode_steps=8, seed=6
             "pages_cached_at_end": pp.cached_pages()}
 
 
+def _short_name(kernel_name: str) -> str:
+    return kernel_name.replace("void ", "", 1).replace("astr::(anonymous namespace)::", "", 1).split("(")[0]
+
+
 def summarize_trace(trace_dir: str):
     """Per-kernel call count, mean and median duration (us) from a rocprofv3
-    --kernel-trace run (its kernel_trace.csv), as a markdown table."""
+    --kernel-trace run (its kernel_trace.csv), one row per kernel and launch
+    size (workgroups), as a markdown table."""
     import csv
     import glob
     rows = {}
     for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
-            name = r["Kernel_Name"].replace("void ", "", 1).replace("astr::(anonymous namespace)::", "", 1)
+            name = _short_name(r["Kernel_Name"])
             if not any(k in name for k in ("decode", "prefill", "rope", "stream_read", "mfma_loop")):
                 continue
-            name = name.split("(")[0]
-            rows.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    print("| kernel | calls | mean | median | min | max |")
-    print("|---|---:|---:|---:|---:|---:|")
-    for name in sorted(rows):
-        v = np.array(rows[name])
-        print(f"| `{name}` | {v.size} | {v.mean():.2f} | {np.median(v):.2f} | {v.min():.2f} | {v.max():.2f} |")
+            wgs = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(
+                1, int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
+            rows.setdefault((name, wgs), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | workgroups | calls | mean | median | min | max |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for name, wgs in sorted(rows):
+        v = np.array(rows[(name, wgs)])
+        print(f"| `{name}` | {wgs} | {v.size} | {v.mean():.2f} | {np.median(v):.2f} | {v.min():.2f} | {v.max():.2f} |")
+
+
+def summarize_counters(pmc_dir: str):
+    """Mean of every counter per kernel and launch size (workgroups) from a
+    rocprofv3 --pmc run, as a markdown table (attention-path kernels only)."""
+    import csv
+    import glob
+    vals, names = {}, []
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = _short_name(r["Kernel_Name"])
+            if not any(k in name for k in ("decode", "prefill", "rope")):
+                continue
+            wgs = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+            c = r["Counter_Name"]
+            if c not in names:
+                names.append(c)
+            vals.setdefault((name, wgs), {}).setdefault(c, {})[int(r["Dispatch_Id"])] = float(r["Counter_Value"])
+    print("| kernel | workgroups | dispatches | " + " | ".join(names) + " |")
+    print("|---|---:|---:|" + "---:|" * len(names))
+    for key in sorted(vals):
+        per = vals[key]
+        n = max(len(per.get(c, {})) for c in names)
+        cells = [f"{np.mean(list(per[c].values())):,.0f}" if c in per else "" for c in names]
+        print(f"| `{key[0]}` | {key[1]} | {n} | " + " | ".join(cells) + " |")
 
 
 def main():
@@ -455,6 +498,9 @@ def main():
                          "known size for calibrating HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="print the mean of each counter per kernel and launch size of a rocprofv3 "
+                         "--pmc run and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print per-kernel call counts, mean and median durations of a rocprofv3 "
                          "--kernel-trace run and exit")
@@ -464,6 +510,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
