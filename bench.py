@@ -314,20 +314,30 @@ def measure_small_configs(stream, dev):
 
 
 def measure_ceilings(stream, dev):
-    """What a plain streaming read (4 GiB, 16-byte loads) and a loop of
-    independent matrix-core products attain on this device."""
+    """What a plain streaming read (4 GiB of random bits, 16-byte loads) and a
+    loop of independent matrix-core products attain on this device.  The read
+    is timed at several grid sizes and the fastest is reported: the rate
+    depends on the grid (8 workgroups per compute unit reads ~10% slower than
+    24 on MI355X), and a ceiling should be the best the chip does."""
     import torch
     import paged_gqa_attention_rope_amd as astr
     n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    buf = torch.ones(1 << 30, dtype=torch.float32, device=dev)            # 4 GiB
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    # random bits, as the attention reads (HBM reads of constant data run ~4% faster)
+    buf = torch.randn(1 << 30, dtype=torch.float32, device=dev, generator=gen)   # 4 GiB
     nbytes = buf.numel() * 4
     res = {}
     for nt in (True, False):
-        wg = 8 * n_cus
-        sink = torch.empty(wg, dtype=torch.int32, device=dev)
-        ms = _rep_ms(lambda: astr.ceiling_stream_read(buf, wg, nt, sink), stream, reps=20)
-        res["stream_read_nt" if nt else "stream_read"] = {
-            "GBps": round(nbytes / (float(np.median(ms)) * 1e-3) / 1e9, 1), "bytes": nbytes, **_stats(ms)}
+        best = None
+        for per_cu in (8, 16, 24, 32):
+            wg = per_cu * n_cus
+            sink = torch.empty(wg, dtype=torch.int32, device=dev)
+            ms = _rep_ms(lambda: astr.ceiling_stream_read(buf, wg, nt, sink), stream, reps=20)
+            gbps = nbytes / (float(np.median(ms)) * 1e-3) / 1e9
+            if best is None or gbps > best["GBps"]:
+                best = {"GBps": round(gbps, 1), "bytes": nbytes, "workgroups": wg, **_stats(ms)}
+        res["stream_read_nt" if nt else "stream_read"] = best
     del buf
     wg, iters = 4 * n_cus, 4096                                           # 4 waves per SIMD
     sink = torch.empty(256 * wg, dtype=torch.float32, device=dev)

@@ -22,9 +22,9 @@ extern "C" {
 #endif
 
 /*
- * Read `bytes` bytes of `buf` once (16-byte loads, grid-stride over
- * `workgroups` workgroups of 256 lanes; non-temporal loads when nontemporal
- * is nonzero).  Each workgroup stores one 32-bit fold of what it read into
+ * Read `bytes` bytes of `buf` once (16-byte loads, eight in flight per lane,
+ * grid-stride over `workgroups` workgroups of 256 lanes; non-temporal loads
+ * when nontemporal is nonzero).  Each workgroup stores one 32-bit fold of what it read into
  * sink[workgroup], so that no load can be elided.
  *   buf    device, 16-byte aligned, `bytes` a positive multiple of 16
  *   sink   device uint32 [workgroups], written

@@ -23,16 +23,17 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
     uint32_t acc = 0;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
     uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    // four independent loads in flight per lane
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        uint4 v[4];
+    // eight independent loads in flight per lane
+    constexpr int U = 8;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        uint4 v[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < U; ++u) {
             if constexpr (NT) v[u] = load_nt16(buf + i + u * stride);
             else v[u] = buf[i + u * stride];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     for (; i < n16; i += stride) {
         uint4 v;
