@@ -335,7 +335,9 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(
     constexpr int RPI = 64 / SL;        // rows per load instruction
     constexpr int NI = CK / RPI;        // load instructions per buffer per chunk
     const int rr = lane / SL, cc = lane % SL;
-    const int32_t *row = req_to_token + static_cast<int64_t>(req) * max_ctx_len;
+    // A request without keys (also one whose row index lies outside the
+    // table, for which L is 0) reads row 0, which always exists.
+    const int32_t *row = req_to_token + static_cast<int64_t>(L > 0 ? req : 0) * max_ctx_len;
     // Every lane reads an entry of the request's row (a key at or past `end`
     // reads entry 0 and is then marked missing): a load without a per-lane
     // branch is one the compiler can count, so the next chunk's index load

@@ -341,6 +341,24 @@ def test_decode_zero_length_request_gives_zero():
     E.assert_close(to_np(out[1]), want[1], "bf16", "request 1")
 
 
+def test_decode_request_row_outside_table_gives_zero():
+    """A batch entry whose request row lies outside req_to_token counts as a
+    request without keys: the kernels never read that row (its output is
+    zero) and the other entry is unaffected."""
+    cs = _dec(43, lens=[40, 70], split_chunk=32)
+    say("decode with a request row outside the table")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    rpi = st.attn_cache.req_pool_indices.clone()
+    rpi[0] = st.attn_cache.req_to_token.shape[0] + 1000
+    c2 = astr.KVCache(**{**st.attn_cache.__dict__, "req_pool_indices": rpi})
+    out = astr.decode_attn(staging.decode_query(st), c2, cs.layer_id, cs.split_chunk)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[0]) == 0
+    want = E.expected_decode(cs, sample=[1])
+    E.assert_close(to_np(out[1]), want[1], "bf16", "request 1")
+
+
 # ---------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------
