@@ -75,7 +75,18 @@ DECODE = {
     "g4-d64-f32-page1": lambda: _dec(18, head_dim=64, dtype="f32", page_size=1, pool_slots=20000),
 }
 
+def _pre_random(s):
+    """Random batch under the library's work plan: extends of 1-700 rows behind
+    shared page-aligned prefixes of up to 1600 tokens; even seeds draw 1-4
+    requests (long tiles dominate and the plan splits them), odd ones 5-24."""
+    rng = np.random.default_rng(900 + s)
+    batch = int(rng.integers(1, 5) if s % 2 == 0 else rng.integers(5, 25))
+    return _pre(500 + s, batch=batch, mode=1, page_size=16, pool_slots=1 << 16, n_groups=3,
+                prefix_pages_hi=100, ext_lo=1, ext_hi=700, shuffle_pages=True)
+
+
 PREFILL = {
+    **{f"plan-random-{s}": (lambda s=s: _pre_random(s)) for s in range(6)},
     "prefill-contig-b4": lambda: make_case(3),
     "prefill-radix-b16": lambda: make_case(4),
     "prefill-radix-b16-seed101": lambda: make_case(4, 101),
