@@ -610,8 +610,16 @@ def main():
     dec_gbs = dbytes / (t_dec * 1e-3) / 1e9
     pre_tfs = pflops / (t_pre * 1e-3) / 1e12
 
-    nxt = configs = ceilings = None
+    nxt = configs = ceilings = back = None
     if not args.no_extras:
+        # the prefill alone, warm: 20 groups of 5 back-to-back calls, one event
+        # pair per group (in the step, the decode's 4.7 GB stream has just
+        # evicted the prefill's keys and values from the caches)
+        say("prefill back to back")
+        groups = _rep_ms(lambda: [staging.run_prefill(st_p, out=out_p) for _ in range(5)], stream, reps=20) / 5
+        back = {"what": "prefill_attn alone, warm caches, 5 calls per event pair", **_stats(groups),
+                "TFLOPs": round(pflops / (float(np.median(groups)) * 1e-3) / 1e12, 1),
+                "frac_of_bf16_peak": round(pflops / (float(np.median(groups)) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
         say("adjacent rows")
         nxt = measure_next_rows(st_d, cs_d, st_p, q_unrot, out_d, o_part, lse_part, stream, dbytes)
         del st_d, o_part, lse_part
@@ -670,6 +678,7 @@ def main():
                                  "ms_per_launch": round(float(t_pre), 5),
                                  "median_ms_per_launch": round(float(m_pre), 5),
                                  "attainable": attainable(pre_tfs, "mfma_bf16_16x16x32", "TFLOPs")},
+                    "back_to_back": back,
                     "plan": {"units": 0 if st_p.attn_cache.prefill_units is None
                              else int(st_p.attn_cache.prefill_units.shape[0]),
                              "split_tiles": int(st_p.attn_cache.num_prefill_pairs)},
