@@ -469,9 +469,26 @@ def summarize_trace(trace_dir: str):
         print(f"| `{name}` | {wgs} | {v.size} | {v.mean():.2f} | {np.median(v):.2f} | {v.min():.2f} | {v.max():.2f} |")
 
 
+def _gpu_agent(pmc_dir: str):
+    """(compute units, XCDs) of the GPU agent from rocprofv3's agent-info file."""
+    import csv
+    import glob
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*agent_info.csv"), recursive=True):
+        for a in csv.DictReader(open(f)):
+            if a.get("Agent_Type", "").upper() == "GPU":
+                return int(a["Cu_Count"]), int(a["Num_Xcc"])
+    return None
+
+
 def summarize_counters(pmc_dir: str):
     """Mean of every counter per kernel and launch size (workgroups) from a
-    rocprofv3 --pmc run, as a markdown table (attention-path kernels only)."""
+    rocprofv3 --pmc run, as a markdown table (attention-path kernels only).
+    Derived columns where their counters were taken: the L2 hit rate
+    TCC_HIT / (TCC_HIT + TCC_MISS), and the mean waves resident per SIMD,
+    SQ_WAVE_CYCLES (quad-cycles summed over all waves) x 4 over the dispatch's
+    active cycles per XCD (GRBM_GUI_ACTIVE, summed over the XCDs) x 4 SIMDs x
+    compute units (rocprof's OccupancyPercent is the same ratio over 32 waves
+    per compute unit)."""
     import csv
     import glob
     vals, names = {}, []
@@ -485,12 +502,24 @@ def summarize_counters(pmc_dir: str):
             if c not in names:
                 names.append(c)
             vals.setdefault((name, wgs), {}).setdefault(c, {})[int(r["Dispatch_Id"])] = float(r["Counter_Value"])
-    print("| kernel | workgroups | dispatches | " + " | ".join(names) + " |")
-    print("|---|---:|---:|" + "---:|" * len(names))
+    agent = _gpu_agent(pmc_dir)
+    hit = "TCC_HIT_sum" in names and "TCC_MISS_sum" in names
+    occ = "SQ_WAVE_CYCLES" in names and "GRBM_GUI_ACTIVE" in names and agent is not None
+    extra = (["L2 hit %"] if hit else []) + (["waves per SIMD"] if occ else [])
+    print("| kernel | workgroups | dispatches | " + " | ".join(names + extra) + " |")
+    print("|---|---:|---:|" + "---:|" * (len(names) + len(extra)))
     for key in sorted(vals):
         per = vals[key]
         n = max(len(per.get(c, {})) for c in names)
-        cells = [f"{np.mean(list(per[c].values())):,.0f}" if c in per else "" for c in names]
+        mean = {c: float(np.mean(list(per[c].values()))) for c in names if c in per}
+        cells = [f"{mean[c]:,.0f}" if c in mean else "" for c in names]
+        if hit:
+            h, m = mean.get("TCC_HIT_sum", 0.0), mean.get("TCC_MISS_sum", 0.0)
+            cells.append(f"{100.0 * h / (h + m):.1f}" if h + m > 0 else "")
+        if occ:
+            cus, xcds = agent
+            active = mean.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+            cells.append(f"{mean.get('SQ_WAVE_CYCLES', 0.0) / (active * cus):.2f}" if active > 0 else "")
         print(f"| `{key[0]}` | {key[1]} | {n} | " + " | ".join(cells) + " |")
 
 

@@ -123,3 +123,29 @@ def test_summarize_counters_means_per_launch_size(tmp_path, capsys):
     assert out[0] == "| kernel | workgroups | dispatches | SQ_INSTS_MFMA | GRBM_GUI_ACTIVE |"
     assert "| `prefill_rs_kernel<4, false>` | 416 | 2 | 200 | 20 |" in out
     assert "| `prefill_rs_kernel<4, false>` | 192 | 1 | 7 | 1 |" in out
+
+
+def test_summarize_counters_derives_l2_hits_and_waves_per_simd(tmp_path, capsys):
+    # 2 XCDs of 4 compute units: GRBM_GUI_ACTIVE 400 summed = 200 active cycles
+    # per XCD; SQ_WAVE_CYCLES 1600 quad-cycles = 6400 wave-cycles over
+    # 200 cycles x 16 SIMDs = 2 waves per SIMD; 30 hits of 40 requests = 75%
+    d = str(tmp_path / "pmc")
+    k = NS + "prefill_rs_kernel<4, false>(int)"
+    rows = [(1, k, 212992, 512, "TCC_HIT_sum", 30.0), (1, k, 212992, 512, "TCC_MISS_sum", 10.0),
+            (1, k, 212992, 512, "SQ_WAVE_CYCLES", 1600.0), (1, k, 212992, 512, "GRBM_GUI_ACTIVE", 400.0)]
+    _counters(d, rows)
+    _csv(os.path.join(d, "run_agent_info.csv"), ["Agent_Type", "Cu_Count", "Num_Xcc"],
+         [("CPU", "0", "0"), ("GPU", "4", "2")])
+    bench.summarize_counters(d)
+    out = capsys.readouterr().out.strip().splitlines()
+    assert out[0].endswith("| L2 hit % | waves per SIMD |")
+    assert out[2].endswith("| 75.0 | 2.00 |")
+
+
+def test_summarize_counters_omits_occupancy_without_agent_info(tmp_path, capsys):
+    d = str(tmp_path / "pmc")
+    k = NS + "prefill_rs_kernel<4, false>(int)"
+    _counters(d, [(1, k, 212992, 512, "SQ_WAVE_CYCLES", 1600.0), (1, k, 212992, 512, "GRBM_GUI_ACTIVE", 400.0)])
+    bench.summarize_counters(d)
+    out = capsys.readouterr().out.strip().splitlines()
+    assert "waves per SIMD" not in out[0]
