@@ -1090,6 +1090,10 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
         }
         wait_copies<0>();
         }
+        // every copy into the ring has landed (each wave waited for its own):
+        // the output waves stage their rows there (the output waves meet this
+        // barrier at the same point)
+        lds_barrier();
         if (pw < 0) return;
         // a split half: hand the running max to the output waves, then take
         // part in the publish / merge barriers (tid 0 keeps the count)
@@ -1182,6 +1186,7 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
         }
         wait_copies<0>();
     }
+    lds_barrier();                                     // the ring is idle (see the score waves)
 
     if (pw >= 0) {
         // One half of a split tile.  Each half leaves its unnormalised state
@@ -1249,19 +1254,37 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
         }
     }
 
-    const int r = r0 + j;
-    if (r < ti.rows) {
+    // The output rows.  A lane holds 4 consecutive d of one row, so storing
+    // from the accumulators writes 16 rows 4 KB apart per instruction, 32
+    // bytes each (the epilogue took ~3.5 us per workgroup).  Instead each
+    // output wave stages its 16 rows, normalised and rounded, in its 16 KB of
+    // the idle ring as 16 rows of 1 KB (the 4 heads side by side, as in out;
+    // 16-byte chunks XOR-swizzled by row within each head), then stores one
+    // whole row per instruction.
+    {
+        uint8_t *stage = ring + rb * (16 * HW * D * 2);
+        static_assert(4 * 16 * HW * D * 2 <= NB * SLOT, "the staged rows fit in the ring");
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
             const float ls = osum[hh][0];
             const float inv = ls > 0.f ? 1.f / ls : 0.f;
-            uint16_t *dst = out + (static_cast<int64_t>(ti.q0 + ti.row0 + r) * n_heads + h0 + hh) * D + 4 * g;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 uint2 w;
                 w.x = cvt_pk_bf16(o[hh][db][0] * inv, o[hh][db][1] * inv);
                 w.y = cvt_pk_bf16(o[hh][db][2] * inv, o[hh][db][3] * inv);
-                *reinterpret_cast<uint2 *>(dst + 16 * db) = w;
+                const int c = 2 * db + (g >> 1);       // 16-byte chunk of row j within head hh
+                *reinterpret_cast<uint2 *>(stage + j * (HW * D * 2) + (hh * 16 + (c ^ j)) * 16 + 8 * (g & 1)) = w;
+            }
+        }
+        wave_lds_fence();
+        // row i: lane l stores bytes 16l .. 16l+15 of the row's 4 heads (chunk
+        // l, staged at l ^ i)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (r0 + i < ti.rows) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(stage + i * (HW * D * 2) + (lane ^ i) * 16);
+                *reinterpret_cast<uint4 *>(out + (static_cast<int64_t>(ti.q0 + ti.row0 + r0 + i) * n_heads + h0) * D + 8 * lane) = v;
             }
         }
     }
