@@ -742,15 +742,18 @@ __device__ __forceinline__ void pin(T (&x)[N]) {
 // needs it (four times per step each); a score wave reads the K operands of
 // step t+1 during step t, after issuing the products of S(t), so that its
 // products start at the barrier instead of behind the burst of LDS reads
-// that follows it (1-3% faster on the radix-prefix, balanced and contiguous
-// batches).  One barrier per step: in iteration t
+// that follows it.  One barrier per step: in iteration t
 // the score waves form P(t) while the output waves consume P(t-1).  A raise
-// of the running max travels with P (a flag and the per-row factors), and
-// the output waves rescale before adding.
+// of the running max travels with P (a flag, set only on a raise and cleared
+// by the output wave that reads it, and the per-row factors), and the output
+// waves rescale before adding.
 // Keys arrive through a ring of 6 LDS slots by asynchronous copies issued 4
-// steps ahead by all 8 waves (slot indices 6 steps ahead); every wait is an
-// explicit count.  Steps are numbered from the unit's first step t0; ring
-// slot and P slot follow t - t0.
+// steps ahead by the 4 output waves (slot indices 6 steps ahead); every wait
+// is an explicit count.  The score waves, which set the pace of a step, issue
+// no copies, and their common path holds only the products, the max test,
+// exp2 and the packing: each vector instruction taken off it measured worth
+// ~15-20 cycles of the step.  Steps are numbered from the unit's first step
+// t0; ring slot and P slot follow t - t0.
 // Q is multiplied by scale*log2(e) and rounded to bf16 once, when it is
 // loaded, and every score accumulator starts at -m (the running max), so the
 // products deliver the exponent itself and P needs only the exp2 and the
@@ -758,7 +761,10 @@ __device__ __forceinline__ void pin(T (&x)[N]) {
 // per element of q; on the radix-prefix batch the relative L2 error against
 // the float64 definition goes from 2.4e-3 to 2.9e-3).  The keys of a step
 // whose slot lies outside the pool are found by one ballot over its 32 slot
-// indices, and the raise test of the running max is one ballot per head.
+// indices, and the raise test of the running max is one ballot: the max of
+// the lane's 32 scores (4 heads) against the smallest of the heads'
+// thresholds (the heads share the rows and the mask, so their thresholds
+// move together; a raise recomputes each head's max).
 // Measured against an earlier design of this kernel, where two groups of 4
 // waves alternated product and vector phases with a barrier per phase: 3-6%
 // faster on 16 requests with radix prefixes, ~2% on 64 requests of 2048
@@ -853,9 +859,17 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
         return ring + R * SLOT;
     };
 
-    // ---- copies (all waves): wave w fills rows 4w .. 4w+3 of a step ----
-    const int crow = RPI * wave + lane / SL;
-    const uint32_t ccol = (WIDE ? 0 : kvh * RB) + 16 * ((lane % SL) ^ swz<D>(crow));
+    // ---- copies (output waves): output wave ow fills rows 8ow .. 8ow+7 of a
+    // step (two wave-wide copies of 4 rows for K and for V) and fetches the
+    // slot indices of those keys ----
+    const int ow = wave & 3;
+    int crow[2];
+    uint32_t ccol[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        crow[c] = 8 * ow + RPI * c + lane / SL;
+        ccol[c] = (WIDE ? 0 : kvh * RB) + 16 * ((lane % SL) ^ swz<D>(crow[c]));
+    }
     const int32_t *trow = req_to_token + static_cast<int64_t>(ti.req) * max_ctx_len;
     const uint32_t slot_lim = static_cast<uint32_t>(min(pool_slots, static_cast<int64_t>(INT32_MAX)));
     const uint32_t stride = WIDE ? RB : static_cast<uint32_t>(n_kv) * RB;
@@ -865,26 +879,34 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
     const i32x4_t krs = buffer_rsrc(k_layer, stride, records);
     const i32x4_t vrs = buffer_rsrc(v_layer, stride, records);
     const i32x4_t trs = buffer_rsrc(trow, 0, 4u * static_cast<uint32_t>(ti.kv_end));
-    const uint32_t idx_voff = 4u * (RPI * wave + lane);
-    const uint32_t sidx_base = lds_addr(sidx) + 4u * RPI * wave;
-    // slot indices of step t's rows 4w .. 4w+3 into index slot t % NI
+    const uint32_t idx_voff = 4u * (8 * ow + lane);
+    const uint32_t sidx_base = lds_addr(sidx) + 4u * 8 * ow;
+    // slot indices of step t's keys 8ow .. 8ow+7 into index slot t % NI
     auto fetch_idx = [&](int t) {
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(sidx_base + 4u * RPI * WAVES * (t & (NI - 1)));
-        if (lane < RPI) copy_raw4_to_lds(trs, idx_voff + 4u * TS * t, dst);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(sidx_base + 4u * TS * (t & (NI - 1)));
+        if (lane < 8) copy_raw4_to_lds(trs, idx_voff + 4u * TS * t, dst);
     };
-    // this lane's row's slot index of step t (its index copy has landed)
-    auto slot_index = [&](int t) -> int32_t { return sidx[t & (NI - 1)][wave][lane / SL]; };
-    // rows of step t into ring slot R (t >= t1, or past the visible keys:
-    // out-of-range records, which read zeros; the copy count never changes)
-    auto issue = [&](auto rc, int t, int32_t sl) {
-        const bool ok = static_cast<uint32_t>(sl) < slot_lim;
-        uint32_t rec;
-        if constexpr (WIDE) rec = ok ? static_cast<uint32_t>(sl) * n_kv + kvh : 0xffffffffu;
-        else rec = static_cast<uint32_t>(sl);
-        if (crow >= kv_lim - TS * t) rec = 0xffffffffu;
-        const uint32_t dk = lds_addr(slot_ptr(rc)) + RB * RPI * wave;
-        copy_record16_to_lds(krs, rec, ccol, dk);
-        copy_record16_to_lds(vrs, rec, ccol, dk + MAT);
+    // this wave's slot indices of step t's rows (their index copies landed)
+    auto slot_index = [&](int t, int32_t (&sl)[2]) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) sl[c] = (&sidx[t & (NI - 1)][0][0])[crow[c]];
+    };
+    // rows of step t into ring slot R with slot indices sl2; t >= t1, or past
+    // the visible keys: out-of-range records, which read zeros (the copy
+    // count never changes)
+    auto issue = [&](auto rc, int t, const int32_t (&sl2)[2]) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int32_t sl = sl2[c];
+            const bool ok = static_cast<uint32_t>(sl) < slot_lim;
+            uint32_t rec;
+            if constexpr (WIDE) rec = ok ? static_cast<uint32_t>(sl) * n_kv + kvh : 0xffffffffu;
+            else rec = static_cast<uint32_t>(sl);
+            if (crow[c] >= kv_lim - TS * t) rec = 0xffffffffu;
+            const uint32_t dk = lds_addr(slot_ptr(rc)) + RB * (8 * ow + RPI * c);
+            copy_record16_to_lds(krs, rec, ccol[c], dk);
+            copy_record16_to_lds(vrs, rec, ccol[c], dk + MAT);
+        }
     };
     // bit k: key k of step t has its slot in the pool (the 32 slot indices of
     // a step lie contiguously in its index slot; every wave's index copy of
@@ -905,31 +927,55 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
         constexpr int P = decltype(pc)::value;
         return pring + P * PSLOT + ((rb * HW + hh) * 64 + lane) * 16;
     };
-    // prologue: indices of steps t0..t0+5, rows of steps t0..t0+3, in the
-    // order that leaves exactly 6 copies after the rows of step t0+2 at the
-    // end of the first iteration (as after the rows of step t+2 at the end of
-    // iteration t); each index copy is waited for by the count issued after it,
-    // and the rows of steps t0 and t0+1 before the barrier
+    if (tid < 8) (&aflag[0][0])[tid] = 0u;          // no raise yet (the prologue's barrier publishes it)
+    // prologue (output waves): indices of steps t0..t0+5, rows of steps
+    // t0..t0+3, in the order that leaves exactly 10 copies after the rows of
+    // step t0+2 at the end of the first iteration (as after the rows of step
+    // t+2 at the end of iteration t); each index copy is waited for by the
+    // count issued after it, and the rows of steps t0 and t0+1 before the
+    // barrier, which the score waves meet
     auto prologue = [&]() {
-        for (int t = t0; t < t0 + 5; ++t) fetch_idx(t);
-        wait_copies<4>();
-        issue(int_c<0>{}, t0, slot_index(t0));
-        wait_copies<5>();
-        issue(int_c<1>{}, t0 + 1, slot_index(t0 + 1));
-        wait_copies<6>();
-        issue(int_c<2>{}, t0 + 2, slot_index(t0 + 2));
-        fetch_idx(t0 + 5);
-        wait_copies<8>();
-        issue(int_c<3>{}, t0 + 3, slot_index(t0 + 3));
-        wait_copies<5>();                              // rows of steps t0 and t0 + 1
+        if (outw) {
+            fetch_idx(t0);
+            fetch_idx(t0 + 1);
+            fetch_idx(t0 + 2);
+            wait_copies<2>();                          // indices of step t0
+            {
+                int32_t sl[2];
+                slot_index(t0, sl);
+                issue(int_c<0>{}, t0, sl);
+            }
+            fetch_idx(t0 + 3);
+            wait_copies<6>();
+            {
+                int32_t sl[2];
+                slot_index(t0 + 1, sl);
+                issue(int_c<1>{}, t0 + 1, sl);
+            }
+            fetch_idx(t0 + 4);
+            wait_copies<10>();
+            {
+                int32_t sl[2];
+                slot_index(t0 + 2, sl);
+                issue(int_c<2>{}, t0 + 2, sl);
+            }
+            fetch_idx(t0 + 5);
+            wait_copies<10>();
+            {
+                int32_t sl[2];
+                slot_index(t0 + 3, sl);
+                issue(int_c<3>{}, t0 + 3, sl);
+            }
+            wait_copies<10>();                         // rows of steps t0 and t0 + 1
+        }
         phase_end();
     };
 
-    // Every iteration t (t0 .. t1, one barrier each): both roles first take
-    // the slot index of step t+4 (its copy landed: 5 copies were issued after
-    // it); after their work, the indices of step t+6 and the rows of step t+4,
-    // then the wait for the rows of step t+2 (6 copies were issued after them;
-    // the score waves read the K operands of step t+1 in iteration t).
+    // Every iteration t (t0 .. t1, one barrier each): the output waves first
+    // take their slot indices of step t+4 (9 copies were issued after them);
+    // after their products, the indices of step t+6 and the rows of step t+4,
+    // then the wait for the rows of step t+2 (10 copies were issued after
+    // them; the score waves read the K operands of step t+1 in iteration t).
     // The two roles run apart (their barriers meet: every wave of the
     // workgroup passes the same number of them in the same order).
     constexpr int64_t kPart = kPrefillPartFloats;
@@ -966,6 +1012,7 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
         // accumulator, so a product's result is already the exponent; thr:
         // accumulator value above which m is raised
         float neg_m[HW], thr[HW];
+        float thr_min = -INFINITY;                     // the smallest of thr
         f32x4_t bias[HW];
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
@@ -997,10 +1044,7 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
         const int s_diag = (qpos0 + 1) / TS;
         auto step = [&](auto rc, int t) -> bool {
             constexpr int R = decltype(rc)::value;
-            constexpr int R4 = (R + 4) % NB;
             constexpr int P = R & 1;
-            wait_copies<5>();
-            const int32_t sl4 = slot_index(t + 4);
             const int32_t nix = idx_of_step(t + 1);
             if (t < t1) {
                 Frag8 (&kf)[KS][2] = (R & 1) ? kB : kA;  // read during step t-1
@@ -1035,16 +1079,32 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
                         }
                     }
                 }
-                float lm[HW];
-                uint64_t fire = 0;
+                // One test for the 4 heads: the max of this lane's 32 scores
+                // against the smallest threshold (a raise is needed only if
+                // some head's max passes its own threshold, which implies this)
+                float lmax;
+                {
+                    // (IEEE maximum: hipcc forms v_maximum3 from these nests)
+                    auto max3 = [](float x, float y, float z) {
+                        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+                    };
+                    float b[HW], c[HW];
 #pragma unroll
-                for (int hh = 0; hh < HW; ++hh) {
-                    lm[hh] = fmaxf(fmaxf(fmaxf(sc[hh][0][0], sc[hh][0][1]), fmaxf(sc[hh][0][2], sc[hh][0][3])),
-                                   fmaxf(fmaxf(sc[hh][1][0], sc[hh][1][1]), fmaxf(sc[hh][1][2], sc[hh][1][3])));
-                    fire |= __builtin_amdgcn_ballot_w64(lm[hh] > thr[hh]);
+                    for (int hh = 0; hh < HW; ++hh) {
+                        const float a = max3(sc[hh][0][0], sc[hh][0][1], sc[hh][0][2]);
+                        b[hh] = max3(sc[hh][0][3], sc[hh][1][0], sc[hh][1][1]);
+                        c[hh] = max3(sc[hh][1][2], sc[hh][1][3], a);
+                    }
+                    const float m1 = max3(b[0], c[0], b[1]), m2 = max3(c[1], b[2], c[2]);
+                    lmax = __builtin_elementwise_maximum(max3(b[3], c[3], m1), m2);
                 }
-                uint32_t flag = 0;
+                const uint64_t fire = __builtin_amdgcn_ballot_w64(lmax > thr_min);
                 if (__builtin_expect(fire != 0, 0)) {
+                    float lm[HW];
+#pragma unroll
+                    for (int hh = 0; hh < HW; ++hh)
+                        lm[hh] = fmaxf(fmaxf(fmaxf(sc[hh][0][0], sc[hh][0][1]), fmaxf(sc[hh][0][2], sc[hh][0][3])),
+                                       fmaxf(fmaxf(sc[hh][1][0], sc[hh][1][1]), fmaxf(sc[hh][1][2], sc[hh][1][3])));
                     // Raise the running max where a score exceeds it by more than
                     // kLazy (exact: the same stale max enters numerator and
                     // denominator, and probabilities stay below 2^8), and hand the
@@ -1054,7 +1114,12 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
                         const float mx = max_over_groups(lm[hh]) - neg_m[hh];   // the row max
                         const float mnew = mx > m[hh] + kLazy ? mx : m[hh];
                         const float alpha = exp2_sub(m[hh], mnew);
-                        m[hh] = mnew;
+                        {                              // in place: no copies on the common path
+                            float x = m[hh];
+                            // (alpha, computed from the old m, is an input: formed first)
+                            asm volatile("v_mov_b32 %0, %1" : "+v"(x) : "v"(mnew), "v"(alpha));
+                            m[hh] = x;
+                        }
                         const float nb = mnew == -INFINITY ? 0.f : -mnew;
                         const float shift = nb - neg_m[hh];
 #pragma unroll
@@ -1069,9 +1134,9 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
                         thr[hh] = mnew == -INFINITY ? -INFINITY : kLazy;
                         if (g == 0) alpha_s[P][rb][hh][j] = alpha;
                     }
-                    flag = 1;
+                    thr_min = fminf(fminf(thr[0], thr[1]), fminf(thr[2], thr[3]));
+                    if (lane == 0) aflag[P][rb] = 1u;  // the output wave clears it after use
                 }
-                if (lane == 0) aflag[P][rb] = flag;
 #pragma unroll
                 for (int hh = 0; hh < HW; ++hh) {
                     float p[2][4];
@@ -1088,10 +1153,7 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
                     *reinterpret_cast<uint4 *>(p_addr(int_c<P>{}, hh)) = w;
                 }
             }
-            fetch_idx(t + 6);
-            issue(int_c<R4>{}, t + 4, sl4);
             okw_cur = ok_bits(nix);
-            wait_copies<6>();                          // rows of step t+2
             phase_end();
             return t >= t1;
         };
@@ -1152,8 +1214,9 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
             constexpr int R = decltype(rc)::value;
             constexpr int R4 = (R + 4) % NB, RP = (R + NB - 1) % NB;   // ring slot of step t-1
             constexpr int P = (R + 1) & 1;                           // P slot of step t-1
-            wait_copies<5>();
-            const int32_t sl4 = slot_index(t + 4);
+            wait_copies<9>();                          // this wave's indices of step t+4
+            int32_t sl4[2];
+            slot_index(t + 4, sl4);
             if (t > t0) {
                 // P(t-1) and V(t-1) (written / landed before the last barrier)
                 const uint32_t fl = aflag[P][rb];
@@ -1167,6 +1230,7 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
                     vf[db].h[1] = lds_read_tr16(reinterpret_cast<const uint16_t *>(vbase + 16 * RB + vofs[db]));
                 }
                 if (__builtin_expect(__builtin_amdgcn_readfirstlane(static_cast<int>(fl)) != 0, 0)) {
+                    if (lane == 0) aflag[P][rb] = 0u;  // read; the score wave sets it again two steps on at the earliest
 #pragma unroll
                     for (int hh = 0; hh < HW; ++hh) {
                         const float a = alpha_s[P][rb][hh][j];
@@ -1187,7 +1251,7 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
             }
             fetch_idx(t + 6);
             issue(int_c<R4>{}, t + 4, sl4);
-            wait_copies<6>();                          // rows of step t+2
+            wait_copies<10>();                         // rows of step t+2
             phase_end();
             return t >= t1;
         };
