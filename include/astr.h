@@ -376,11 +376,11 @@ size_t astr_prefill_workspace_bytes(int pairs, int n_heads, int head_dim);
  * (only tiles with n_t >= 2 are cut).  For each, the units are listed by decreasing cost (ties: tile
  * order, then lower half first) and dealt to the 8 XCDs in that order,
  * each to an XCD where it would end first; among those, an XCD that already
- * holds one or two units of the same batch entry comes first, then fewer
+ * holds one to three units of the same batch entry comes first, then fewer
  * units queued, then the lower XCD.  A request's tiles all read its
  * page-aligned key/value prefix (inference.md, "KVCache System") and each
  * XCD has its own L2, so tiles kept together fetch the prefix fewer times;
- * at most three per XCD, as more tiles of one request running side by side
+ * at most four per XCD, as more tiles of one request running side by side
  * on one XCD measured slower.  An XCD runs its queue in order on num_cus / 8 compute units,
  * one workgroup per compute unit, the unit's workgroups_per_tile workgroups
  * on the ones free first.  The candidate with the earliest simulated end

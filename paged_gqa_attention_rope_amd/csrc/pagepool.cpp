@@ -564,7 +564,7 @@ constexpr double kWhole = 7.0;             // per whole tile: prologue and outpu
 constexpr double kLower = 8.5;             // lower half: prologue and publishing its state
 constexpr double kUpper = 9.5;             // upper half: prologue, merge and output
 constexpr double kEmpty = 0.1;             // a tile the kernel skips
-constexpr int kJoinCap = 3;                // most units of one request an XCD takes by preference
+constexpr int kJoinCap = 4;                // most units of one request an XCD takes by preference
 
 struct PlanUnit {
     double cost;

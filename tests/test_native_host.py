@@ -502,7 +502,7 @@ def _plan_rule(meta, wg, num_cus):
         return sorted(out, key=lambda u: (-u[0], u[1], u[2]))
 
     def deal(lst):
-        # earliest end; on ties an XCD holding 1 or 2 units of the same
+        # earliest end; on ties an XCD holding 1 to 3 units of the same
         # request first, then fewer units queued, then the lower XCD
         free = [[0.0] * (num_cus // 8) for _ in range(8)]
         queue = [[] for _ in range(8)]
@@ -512,7 +512,7 @@ def _plan_rule(meta, wg, num_cus):
         for u in lst:
             ends = [sorted(free[x])[w - 1] + u[0] for x in range(8)]
             grp = group[u[1]]
-            joins = [grp >= 0 and 0 < holds[x].get(grp, 0) < 3 for x in range(8)]
+            joins = [grp >= 0 and 0 < holds[x].get(grp, 0) < 4 for x in range(8)]
             x = min(range(8), key=lambda x: (ends[x], 0 if joins[x] else 1, len(queue[x]), x))
             if grp >= 0:
                 holds[x][grp] = holds[x].get(grp, 0) + 1
