@@ -776,7 +776,7 @@ struct RsCfg {
     static constexpr int SLOT = 2 * MAT;               // one step's K rows, then its V rows
     static constexpr int RPI = 1024 / RB;              // rows one wave-wide 16-byte copy fills
     static constexpr int PSLOT = 4 * HW * 64 * 16;     // one step's P of the 4 score waves
-    static_assert(RPI * WAVES == TS, "one K and one V copy per wave and step");
+    static_assert(2 * RPI * (WAVES / 2) == TS, "two K and two V copies per output wave and step");
 };
 
 template <int G, bool WIDE>
