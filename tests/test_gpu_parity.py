@@ -429,6 +429,61 @@ def test_prefill_keys_outside_pool_take_no_part(name):
         E.assert_close(got[off[b]:off[b + 1]], want[b], cs.dtype, f"{name} request {b}")
 
 
+def _with_score_jumps(cs, rng):
+    """Scale two cached prefix keys of every prefix group by 2^4 and 2^7
+    (exact in bf16), at random positions past the first quarter of the
+    prefix: rows that reach them see their running maximum jump by tens to
+    hundreds in the exponent, past the range of a float exponential."""
+    orig = cs._group_hist
+    picks = {}
+    for grp, toks in enumerate(cs.group_tokens):
+        n = len(toks)
+        if n >= 8:
+            picks[grp] = rng.choice(np.arange(n // 4, n), size=2, replace=False)
+
+    def hist(grp):
+        k, v = orig(grp)
+        if grp in picks:
+            k = k.copy()
+            k[picks[grp][0]] *= 16.0
+            k[picks[grp][1]] *= 128.0
+        return k, v
+    cs._group_hist = hist
+    return sum(len(p) for p in picks.values())
+
+
+@pytest.mark.parametrize("name", ["prefill-radix-b16", "prefix-g8-d128", "prefix-g6-d64", "prefix-page16-g1-d64"])
+def test_prefill_score_jumps_raise_the_max(name):
+    # The lazily raised running max (softmax over the visible keys, AstrAI
+    # docs/guides/inference.md, 'Attention Backend') must follow scores that
+    # jump far past it midway through a row.  The bf16 kernels take
+    # q * scale * log2(e) rounded to bf16 as the product operand; with a
+    # 2^7-scaled key that rounding alone moves a score by ~0.2 in the
+    # exponent, so this test uses the softmax scale for which that factor is
+    # 1/8 (exact); the query operand is the oracle's stored rotation (a
+    # 1-ulp rounding difference of the rotation would be scaled by 2^7 as
+    # well), so the comparison checks the running max.
+    cs = PREFILL[name]()
+    n = _with_score_jumps(cs, np.random.default_rng(cs.seed + 11))
+    assert n > 0
+    scale = float(np.float32(0.125 / math.log2(math.e)))
+    say(f"prefill with score jumps, case={name} seed={cs.seed} scaled keys={n} scale={scale:.8f}")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    q_rot, k_rot = E.rotated_new(cs)
+    q_in = torch.from_numpy(q_rot.astype(np.float32)).to(st.q.dtype).cuda()
+    assert q_in.shape == st.q.shape
+    out = astr.prefill_attn(q_in, st.attn_cache, cs.layer_id, sm_scale=scale)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    off = E.new_offsets(cs)
+    for b in range(cs.batch):
+        K, V = E.request_kv(cs, b, k_rot)
+        want = A.prefill_dense(q_rot[off[b]:off[b + 1]], K, V, scale, None)
+        assert np.all(np.isfinite(want))
+        E.assert_close(got[off[b]:off[b + 1]], want, cs.dtype, f"{name} request {b}")
+
+
 @pytest.mark.parametrize("name", ["decode-page1-b8", "g8-d128", "g6-d64", "g2-d128-f32", "length-one-and-two"])
 def test_decode_keys_outside_pool_take_no_part(name):
     cs = DECODE[name]()
