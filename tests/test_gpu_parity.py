@@ -484,6 +484,52 @@ def test_prefill_score_jumps_raise_the_max(name):
         E.assert_close(got[off[b]:off[b + 1]], want, cs.dtype, f"{name} request {b}")
 
 
+@pytest.mark.parametrize("name", ["decode-page1-b8", "page16-3layers-chunk512", "g8-d128", "g6-d64"])
+def test_decode_score_jumps_across_splits(name):
+    # Split-K partials whose log-sum-exps differ by up to ~185 in the
+    # exponent must merge to the direct softmax (AstrAI
+    # docs/guides/inference.md, 'KVCache System': partial outputs with their
+    # max and sum).  Two cached keys per request are scaled by 2^4 and 2^7
+    # (exact in bf16).  The query operand is the oracle's stored rotation (a
+    # 1-ulp difference of the rotation would be scaled by 2^7); the softmax
+    # scale is the prefill test's (this kernel scales its float32 scores, so
+    # any scale would do).
+    cs = DECODE[name]()
+    rng = np.random.default_rng(cs.seed + 11)
+    orig = cs._hist
+    picks = {}
+    for b in range(cs.batch):
+        n = int(cs.hist_lens[b])
+        if n >= 8:
+            picks[b] = rng.choice(np.arange(n // 4, n), size=2, replace=False)
+
+    def hist(b):
+        k, v = orig(b)
+        if b in picks:
+            k = k.copy()
+            k[picks[b][0]] *= 16.0
+            k[picks[b][1]] *= 128.0
+        return k, v
+    cs._hist = hist
+    assert picks
+    scale = float(np.float32(0.125 / math.log2(math.e)))
+    say(f"decode with score jumps, case={name} seed={cs.seed} requests with scaled keys={len(picks)}")
+    st = staging.stage(cs)
+    staging.run_write(st)
+    q_rot, k_rot = E.rotated_new(cs)
+    off = E.new_offsets(cs)
+    last = [int(off[b + 1]) - 1 for b in range(cs.batch)]
+    q_in = torch.from_numpy(q_rot[last].astype(np.float32)).to(st.q.dtype).cuda()
+    out = astr.decode_attn(q_in, st.attn_cache, cs.layer_id, cs.split_chunk, sm_scale=scale)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    for b in range(cs.batch):
+        K, V = E.request_kv(cs, b, k_rot)
+        want = A.decode_dense(q_rot[last[b]], K, V, scale, None)
+        assert np.all(np.isfinite(want))
+        E.assert_close(got[b], want, cs.dtype, f"{name} request {b} (L={cs.seq_lens[b]})")
+
+
 @pytest.mark.parametrize("name", ["decode-page1-b8", "g8-d128", "g6-d64", "g2-d128-f32", "length-one-and-two"])
 def test_decode_keys_outside_pool_take_no_part(name):
     cs = DECODE[name]()
