@@ -846,6 +846,11 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
     const int t0 = step_lo;
     const int t1 = min(step_hi, (ti.kv_end + TS - 1) / TS);
     const int kv_lim = min(ti.kv_end, TS * t1);
+    // This wave pair's own steps [t0, t1w): every key of a later step lies
+    // past the last of its rows (causal mask), and rows past the tile's end
+    // have no steps, so those products and exponentials would only add zeros.
+    // The pair still takes part in every copy and barrier up to t1.
+    const int t1w = r0 < ti.rows ? min(t1, (ti.p + ti.row0 + min(r0 + 15, ti.rows - 1)) / TS + 1) : t0;
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NB * SLOT];
     __shared__ __attribute__((aligned(16))) uint8_t pring[2 * PSLOT];   // P of steps t - t0 = 0, 1 mod 2
@@ -1046,7 +1051,7 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
             constexpr int R = decltype(rc)::value;
             constexpr int P = R & 1;
             const int32_t nix = idx_of_step(t + 1);
-            if (t < t1) {
+            if (t < t1w) {
                 Frag8 (&kf)[KS][2] = (R & 1) ? kB : kA;  // read during step t-1
                 Frag8 (&kn)[KS][2] = (R & 1) ? kA : kB;
                 f32x4_t sc[HW][2];
@@ -1217,7 +1222,7 @@ __global__ __launch_bounds__(RsCfg::THREADS, 1) void prefill_rs_kernel(
             wait_copies<9>();                          // this wave's indices of step t+4
             int32_t sl4[2];
             slot_index(t + 4, sl4);
-            if (t > t0) {
+            if (t > t0 && t <= t1w) {
                 // P(t-1) and V(t-1) (written / landed before the last barrier)
                 const uint32_t fl = aflag[P][rb];
                 Frag8 pf[HW], vf[DB];
